@@ -1,0 +1,334 @@
+"""Python binding of libdllm_commit (the dLLM commit step on MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+library ``libdllm_commit.so`` next to this file.  PyTorch provides device
+memory and the current stream.  There is no CPU fallback: if the library is
+not built, every call raises.
+
+Names and keyword arguments follow mlx-arsenal's ``mlx_arsenal.diffusion``
+functions ("dLLM block decoding", "What mlx-arsenal ships"): token_stats,
+threshold_transfer, topk_transfer, factor_transfer, entropy_bound_transfer,
+edit_transfer, transfer_schedule, block_ranges, block_causal_mask.
+"""
+import ctypes
+import os
+from collections import namedtuple
+
+import torch
+
+__all__ = ["Stats", "Rule", "token_stats", "threshold_transfer", "topk_transfer",
+           "factor_transfer", "entropy_bound_transfer", "edit_transfer",
+           "transfer_schedule", "block_ranges", "block_causal_mask",
+           "workspace_size", "library_path", "load_library"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libdllm_commit.so")
+
+DLLM_F32, DLLM_BF16 = 0, 1
+RULE_THRESHOLD, RULE_TOPK, RULE_FACTOR, RULE_ENTROPY_BOUND, RULE_EDIT = 1, 2, 3, 4, 5
+MAX_L = 4096
+MAX_SUPPRESS = 64
+
+Stats = namedtuple("Stats", ["x0", "prob", "entropy"])
+
+
+class _CRule(ctypes.Structure):
+    _fields_ = [("kind", ctypes.c_int), ("mask", ctypes.c_void_p), ("out", ctypes.c_void_p),
+                ("param", ctypes.c_double), ("strict", ctypes.c_int),
+                ("k", ctypes.c_void_p), ("tokens", ctypes.c_void_p)]
+
+
+_lib = None
+
+# The exported C entry points and their signatures (include/dllm_commit.h).
+_I64, _I32, _P = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+_SIGNATURES = {
+    "dllm_token_stats": (_I32, [_P, _I32, _I64, _I64, _I64, _I64, ctypes.c_float, ctypes.c_uint64,
+                                ctypes.c_uint64, _P, _I32, _P, _P, _P, _P, _I32, _P,
+                                ctypes.c_size_t, _P]),
+    "dllm_token_stats_workspace_size": (ctypes.c_size_t, [_I32, _I64, _I64, _I64]),
+    "dllm_transfer_threshold": (_I32, [_P, _P, _I64, _I64, ctypes.c_double, _I32, _P, _P]),
+    "dllm_transfer_topk": (_I32, [_P, _P, _P, _I64, _I64, _P, _P]),
+    "dllm_transfer_factor": (_I32, [_P, _P, _I64, _I64, ctypes.c_double, _P, _P]),
+    "dllm_transfer_entropy_bound": (_I32, [_P, _P, _I64, _I64, ctypes.c_double, _P, _P]),
+    "dllm_transfer_edit": (_I32, [_P, _P, _P, _P, _I64, _I64, ctypes.c_double, _P, _P]),
+    "dllm_transfer_schedule": (_I32, [_P, _I64, ctypes.c_int32, _P, _P]),
+    "dllm_block_ranges": (_I64, [_I64, _I64, _I64, _I32, _P, _I64]),
+    "dllm_block_causal_mask": (_I32, [_I64, _I64, _P, _P]),
+    "dllm_last_error": (ctypes.c_char_p, []),
+}
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libdllm_commit.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is not built; run `python -m commit_step_amd.build`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(status, what):
+    if status < 0:
+        msg = load_library().dllm_last_error().decode(errors="replace")
+        raise ValueError(f"{what} failed with status {status}: {msg}")
+    return status
+
+
+def _stream(t):
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dev(t, name):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    return t
+
+
+def _bl(t, name, dtypes, shape=None):
+    _dev(t, name)
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} must have dtype in {dtypes}, not {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+    return t
+
+
+_MASK_DTYPES = (torch.bool, torch.uint8)
+_workspaces = {}
+
+
+def workspace_size(logits):
+    B, L, V = logits.shape
+    dt = DLLM_BF16 if logits.dtype == torch.bfloat16 else DLLM_F32
+    with torch.cuda.device(logits.device):
+        return int(load_library().dllm_token_stats_workspace_size(dt, B, L, V))
+
+
+def _workspace(device, nbytes):
+    """A zero-filled byte buffer per device, grown on demand.  The library
+    leaves it zero-filled after every successful call."""
+    key = (device.type, device.index)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+class Rule:
+    """A commit rule fused into token_stats (same launch).
+
+    Build with Rule.threshold / topk / factor / entropy_bound / edit; the
+    result lands in ``rule.out`` (a bool (B, L) tensor).
+    """
+
+    def __init__(self, kind, mask, param=0.0, strict=False, k=None, tokens=None, out=None):
+        self.kind, self.mask, self.param, self.strict = kind, mask, float(param), bool(strict)
+        self.k, self.tokens, self.out = k, tokens, out
+
+    @classmethod
+    def threshold(cls, candidates, tau, strict=False):
+        return cls(RULE_THRESHOLD, candidates, tau, strict=strict)
+
+    @classmethod
+    def topk(cls, candidates, k):
+        return cls(RULE_TOPK, candidates, k=k)
+
+    @classmethod
+    def factor(cls, candidates, f):
+        return cls(RULE_FACTOR, candidates, f)
+
+    @classmethod
+    def entropy_bound(cls, candidates, gamma):
+        return cls(RULE_ENTROPY_BOUND, candidates, gamma)
+
+    @classmethod
+    def edit(cls, editable, tokens, tau_edit):
+        return cls(RULE_EDIT, editable, tau_edit, tokens=tokens)
+
+
+def _k_tensor(k, B, device):
+    if isinstance(k, torch.Tensor):
+        return _bl(k, "k", (torch.int32,), (B,))
+    return torch.full((B,), int(k), dtype=torch.int32, device=device)
+
+
+def token_stats(logits, temperature=0.0, seed=None, step=0, suppress_ids=(), rules=(),
+                out=None, workspace=None):
+    """Per-position (x0, prob, entropy) of (B, L, V) float32 / bfloat16 logits.
+
+    temperature > 0 draws x0 by Gumbel-max and then needs an explicit ``seed``
+    (an integer key; ``step`` selects the per-step noise).  ``rules`` is a list
+    of up to two Rule objects run in the same launch; their ``out`` tensors
+    are filled.  ``out`` may give preallocated (x0, prob, entropy) tensors.
+    """
+    _dev(logits, "logits")
+    if logits.dim() != 3:
+        raise ValueError("logits must be (B, L, V)")
+    if logits.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("logits must be float32 or bfloat16")
+    B, L, V = logits.shape
+    if logits.stride(2) != 1 or logits.stride(0) != L * logits.stride(1):
+        raise ValueError("logits rows must be contiguous and evenly strided")
+    if temperature > 0 and seed is None:
+        raise ValueError("sampling (temperature > 0) needs an explicit seed")
+    dev = logits.device
+    if out is None:
+        x0 = torch.empty((B, L), dtype=torch.int32, device=dev)
+        prob = torch.empty((B, L), dtype=torch.float32, device=dev)
+        ent = torch.empty((B, L), dtype=torch.float32, device=dev)
+    else:
+        x0, prob, ent = out
+        _bl(x0, "x0", (torch.int32,), (B, L))
+        _bl(prob, "prob", (torch.float32,), (B, L))
+        _bl(ent, "entropy", (torch.float32,), (B, L))
+    sup = (ctypes.c_int32 * max(len(suppress_ids), 1))(*[int(s) for s in suppress_ids])
+    crules = (_CRule * 2)()
+    keep = []
+    for i, r in enumerate(rules):
+        _bl(r.mask, "rule mask", _MASK_DTYPES, (B, L))
+        if r.out is None:
+            r.out = torch.empty((B, L), dtype=torch.bool, device=dev)
+        _bl(r.out, "rule out", _MASK_DTYPES, (B, L))
+        c = crules[i]
+        c.kind, c.mask, c.out = r.kind, r.mask.data_ptr(), r.out.data_ptr()
+        c.param, c.strict = r.param, int(r.strict)
+        if r.kind == RULE_TOPK:
+            kt = _k_tensor(r.k, B, dev)
+            keep.append(kt)
+            c.k = kt.data_ptr()
+        if r.kind == RULE_EDIT:
+            _bl(r.tokens, "tokens", (torch.int32,), (B, L))
+            c.tokens = r.tokens.data_ptr()
+    dt = DLLM_BF16 if logits.dtype == torch.bfloat16 else DLLM_F32
+    lib = load_library()
+    with torch.cuda.device(dev):
+        need = int(lib.dllm_token_stats_workspace_size(dt, B, L, V))
+        ws = workspace if workspace is not None else _workspace(dev, need)
+        _check(lib.dllm_token_stats(
+            logits.data_ptr(), dt, B, L, V, logits.stride(1), float(temperature),
+            int(seed or 0) & 0xFFFFFFFFFFFFFFFF, int(step), sup, len(suppress_ids),
+            x0.data_ptr(), prob.data_ptr(), ent.data_ptr(),
+            crules if len(rules) else None, len(rules), ws.data_ptr(), ws.numel(),
+            _stream(logits)), "dllm_token_stats")
+    return Stats(x0, prob, ent)
+
+
+def _rule_out(conf, candidates, out):
+    B, L = conf.shape
+    _bl(candidates, "candidates", _MASK_DTYPES, (B, L))
+    if out is None:
+        out = torch.empty((B, L), dtype=torch.bool, device=conf.device)
+    return _bl(out, "out", _MASK_DTYPES, (B, L))
+
+
+def threshold_transfer(prob, candidates, threshold, strict=False, out=None):
+    """Commit candidates with prob >= threshold (> when strict); force one if none pass."""
+    _bl(prob, "prob", (torch.float32,))
+    out = _rule_out(prob, candidates, out)
+    B, L = prob.shape
+    with torch.cuda.device(prob.device):
+        _check(load_library().dllm_transfer_threshold(
+            prob.data_ptr(), candidates.data_ptr(), B, L, float(threshold), int(bool(strict)),
+            out.data_ptr(), _stream(prob)), "dllm_transfer_threshold")
+    return out
+
+
+def topk_transfer(prob, candidates, k, out=None):
+    """Commit the k[b] most confident candidates of every batch row."""
+    _bl(prob, "prob", (torch.float32,))
+    out = _rule_out(prob, candidates, out)
+    B, L = prob.shape
+    kt = _k_tensor(k, B, prob.device)
+    with torch.cuda.device(prob.device):
+        _check(load_library().dllm_transfer_topk(
+            prob.data_ptr(), candidates.data_ptr(), kt.data_ptr(), B, L, out.data_ptr(),
+            _stream(prob)), "dllm_transfer_topk")
+    return out
+
+
+def factor_transfer(prob, candidates, factor, out=None):
+    """Commit the longest confidence-sorted prefix with (i+1)(1 - c_(i)) <= factor."""
+    _bl(prob, "prob", (torch.float32,))
+    out = _rule_out(prob, candidates, out)
+    B, L = prob.shape
+    with torch.cuda.device(prob.device):
+        _check(load_library().dllm_transfer_factor(
+            prob.data_ptr(), candidates.data_ptr(), B, L, float(factor), out.data_ptr(),
+            _stream(prob)), "dllm_transfer_factor")
+    return out
+
+
+def entropy_bound_transfer(entropy, candidates, gamma, out=None):
+    """Commit the longest entropy-sorted prefix with sum_{j<i} H_(j) <= gamma."""
+    _bl(entropy, "entropy", (torch.float32,))
+    out = _rule_out(entropy, candidates, out)
+    B, L = entropy.shape
+    with torch.cuda.device(entropy.device):
+        _check(load_library().dllm_transfer_entropy_bound(
+            entropy.data_ptr(), candidates.data_ptr(), B, L, float(gamma), out.data_ptr(),
+            _stream(entropy)), "dllm_transfer_entropy_bound")
+    return out
+
+
+def edit_transfer(x0, prob, tokens, editable, editing_threshold, out=None):
+    """edit = editable & (x0 != tokens) & (prob > editing_threshold)."""
+    _bl(prob, "prob", (torch.float32,))
+    B, L = prob.shape
+    _bl(x0, "x0", (torch.int32,), (B, L))
+    _bl(tokens, "tokens", (torch.int32,), (B, L))
+    out = _rule_out(prob, editable, out)
+    with torch.cuda.device(prob.device):
+        _check(load_library().dllm_transfer_edit(
+            x0.data_ptr(), prob.data_ptr(), tokens.data_ptr(), editable.data_ptr(), B, L,
+            float(editing_threshold), out.data_ptr(), _stream(prob)), "dllm_transfer_edit")
+    return out
+
+
+def transfer_schedule(n_masked, steps, out=None):
+    """(B, steps) int32 quotas spreading n_masked[b] evenly, extras first."""
+    _bl(n_masked, "n_masked", (torch.int32,))
+    B = n_masked.shape[0]
+    if out is None:
+        out = torch.empty((B, int(steps)), dtype=torch.int32, device=n_masked.device)
+    _bl(out, "out", (torch.int32,), (B, int(steps)))
+    with torch.cuda.device(n_masked.device):
+        _check(load_library().dllm_transfer_schedule(
+            n_masked.data_ptr(), B, int(steps), out.data_ptr(), _stream(n_masked)),
+            "dllm_transfer_schedule")
+    return out
+
+
+def block_ranges(prompt_len, gen_len, block_len, align=False):
+    """List of (start, end) blocks covering [prompt_len, prompt_len + gen_len)."""
+    lib = load_library()
+    n = _check(lib.dllm_block_ranges(int(prompt_len), int(gen_len), int(block_len),
+                                     int(bool(align)), None, 0), "dllm_block_ranges")
+    buf = (ctypes.c_int64 * max(2 * n, 2))()
+    _check(lib.dllm_block_ranges(int(prompt_len), int(gen_len), int(block_len),
+                                 int(bool(align)), buf, n), "dllm_block_ranges")
+    return [(buf[2 * i], buf[2 * i + 1]) for i in range(n)]
+
+
+def block_causal_mask(L, block_len, device="cuda", out=None):
+    """(L, L) float32 additive mask: 0 within and below the query's block, -inf above."""
+    if out is None:
+        out = torch.empty((int(L), int(L)), dtype=torch.float32, device=device)
+    _bl(out, "out", (torch.float32,), (int(L), int(L)))
+    with torch.cuda.device(out.device):
+        _check(load_library().dllm_block_causal_mask(int(L), int(block_len), out.data_ptr(),
+                                                     _stream(out)), "dllm_block_causal_mask")
+    return out

@@ -1,0 +1,210 @@
+// Shared host and device helpers of libdllm_commit (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dllm_commit.h"
+
+namespace dllm {
+
+// ---------------------------------------------------------------- host side
+
+// Records a printf-style message for dllm_last_error() and returns `code`.
+int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+// Clears the message; returns DLLM_OK.
+int ok();
+// DLLM_ERR_HIP with a message if the last launch failed, else DLLM_OK.
+int check_launch(const char *what);
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
+
+// ---------------------------------------------------------------- wave64 reductions
+// DPP patterns of the GFX9 family: quad_perm, row_half_mirror, row_mirror and the
+// row broadcasts 15 / 31 combine all 64 lanes in six VALU steps; lane 63 ends up
+// with the full result, which readlane makes wave-uniform.
+
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ int dpp_i(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xF, false);
+}
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f(float old, float v) {
+  return __int_as_float(dpp_i<CTRL, ROW_MASK>(__float_as_int(old), __float_as_int(v)));
+}
+
+constexpr int kQuadSwap1 = 0xB1;   // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;   // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+constexpr int kRowBcast15 = 0x142;
+constexpr int kRowBcast31 = 0x143;
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f<kQuadSwap1>(v, v));
+  v = fmaxf(v, dpp_f<kQuadSwap2>(v, v));
+  v = fmaxf(v, dpp_f<kRowHalfMirror>(v, v));
+  v = fmaxf(v, dpp_f<kRowMirror>(v, v));
+  v = fmaxf(v, dpp_f<kRowBcast15, 0xA>(-__builtin_inff(), v));
+  v = fmaxf(v, dpp_f<kRowBcast31, 0xC>(-__builtin_inff(), v));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_f<kQuadSwap1>(v, v);
+  v += dpp_f<kQuadSwap2>(v, v);
+  v += dpp_f<kRowHalfMirror>(v, v);
+  v += dpp_f<kRowMirror>(v, v);
+  v += dpp_f<kRowBcast15, 0xA>(0.0f, v);
+  v += dpp_f<kRowBcast31, 0xC>(0.0f, v);
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+__device__ __forceinline__ int wave_sum_i(int v) {
+  v += dpp_i<kQuadSwap1>(v, v);
+  v += dpp_i<kQuadSwap2>(v, v);
+  v += dpp_i<kRowHalfMirror>(v, v);
+  v += dpp_i<kRowMirror>(v, v);
+  v += dpp_i<kRowBcast15, 0xA>(0, v);
+  v += dpp_i<kRowBcast31, 0xC>(0, v);
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+__device__ __forceinline__ int wave_min_i(int v) {
+  v = min(v, dpp_i<kQuadSwap1>(v, v));
+  v = min(v, dpp_i<kQuadSwap2>(v, v));
+  v = min(v, dpp_i<kRowHalfMirror>(v, v));
+  v = min(v, dpp_i<kRowMirror>(v, v));
+  v = min(v, dpp_i<kRowBcast15, 0xA>(0x7fffffff, v));
+  v = min(v, dpp_i<kRowBcast31, 0xC>(0x7fffffff, v));
+  return __builtin_amdgcn_readlane(v, 63);
+}
+
+// ---------------------------------------------------------------- float helpers
+
+__device__ __host__ __forceinline__ bool bits_finite(uint32_t u) {
+  return (u & 0x7f800000u) != 0x7f800000u;
+}
+
+// Order-preserving map of float32 bits to uint32 (ascending), after
+// canonicalising -0 to +0.  NaN must have been replaced beforehand.
+__device__ __forceinline__ uint32_t sortable_asc(uint32_t u) {
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ uint32_t unsortable_asc(uint32_t s) {
+  return (s & 0x80000000u) ? (s & 0x7fffffffu) : ~s;
+}
+
+// A confidence ranks best-first: NaN counts as -inf.
+__device__ __forceinline__ uint32_t conf_key(float c) {
+  uint32_t u = __float_as_uint(c);
+  if ((u & 0x7fffffffu) > 0x7f800000u) u = 0xff800000u;   // NaN -> -inf
+  return ~sortable_asc(u);
+}
+__device__ __forceinline__ float conf_from_key(uint32_t k) {
+  return __uint_as_float(unsortable_asc(~k));
+}
+// An entropy ranks lowest-first: NaN counts as +inf.
+__device__ __forceinline__ uint32_t ent_key(float h) {
+  uint32_t u = __float_as_uint(h);
+  if ((u & 0x7fffffffu) > 0x7f800000u) u = 0x7f800000u;   // NaN -> +inf
+  return sortable_asc(u);
+}
+__device__ __forceinline__ float ent_from_key(uint32_t k) {
+  return __uint_as_float(unsortable_asc(k));
+}
+__device__ __forceinline__ float conf_sanitized(float c) {
+  uint32_t u = __float_as_uint(c);
+  return ((u & 0x7fffffffu) > 0x7f800000u) ? -__builtin_inff() : c;
+}
+
+// ---------------------------------------------------------------- Philox4x32-10
+// J. K. Salmon, M. A. Moraes, R. O. Dror, D. E. Shaw, "Parallel Random Numbers:
+// As Easy as 1, 2, 3" (SC'11): ten rounds of two 32x32->64 products on the even
+// counter words, xor-mixed with the odd words and the key, the key bumped by
+// the Weyl constants after every round.
+struct Philox4 { uint32_t w[4]; };
+
+__device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
+                                                 uint32_t c3, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
+    const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+    c0 = hi1 ^ c1 ^ k0;
+    c1 = lo1;
+    c2 = hi0 ^ c3 ^ k1;
+    c3 = lo0;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  Philox4 o;
+  o.w[0] = c0; o.w[1] = c1; o.w[2] = c2; o.w[3] = c3;
+  return o;
+}
+
+// Gumbel(0,1) draw from one Philox word: u = ((w >> 9) + 0.5) * 2^-23 (exact in
+// float32), g = -ln(-ln u) with the hardware base-2 logarithm.
+__device__ __forceinline__ float gumbel_from_word(uint32_t w) {
+  const float u = fmaf((float)(w >> 9), 0x1p-23f, 0x1p-24f);
+  const float a = -__builtin_amdgcn_logf(u);          // -log2 u > 0
+  return -kLn2 * __builtin_amdgcn_logf(a * kLn2);     // -ln(-ln u)
+}
+
+// ---------------------------------------------------------------- exact sums
+// A float32 value is m * 2^(E) with a 24-bit integer m and E >= -149, so every
+// finite float32, and every sum of up to 2^12 of them, is an integer multiple
+// of 2^-149 below 2^290 in magnitude: five 64-bit limbs (two's complement) hold
+// such sums exactly, and they add associatively.
+struct Fx { uint64_t w[5]; };
+
+__device__ __host__ __forceinline__ void fx_zero(Fx &a) {
+  for (int i = 0; i < 5; ++i) a.w[i] = 0;
+}
+__device__ __host__ __forceinline__ void fx_add(Fx &a, const Fx &b) {
+  uint64_t carry = 0;
+  for (int i = 0; i < 5; ++i) {
+    const uint64_t s = a.w[i] + b.w[i];
+    const uint64_t c1 = s < a.w[i];
+    const uint64_t t = s + carry;
+    const uint64_t c2 = t < s;
+    a.w[i] = t;
+    carry = c1 | c2;
+  }
+}
+__device__ __host__ __forceinline__ void fx_negate(Fx &a) {
+  uint64_t carry = 1;
+  for (int i = 0; i < 5; ++i) {
+    const uint64_t t = ~a.w[i] + carry;
+    carry = (carry && t == 0) ? 1 : 0;
+    a.w[i] = t;
+  }
+}
+// Signed a <= b.
+__device__ __host__ __forceinline__ bool fx_le(const Fx &a, const Fx &b) {
+  const int64_t ta = (int64_t)a.w[4], tb = (int64_t)b.w[4];
+  if (ta != tb) return ta < tb;
+  for (int i = 3; i >= 0; --i)
+    if (a.w[i] != b.w[i]) return a.w[i] < b.w[i];
+  return true;
+}
+// Exact fixed-point value of a finite float32 (units of 2^-149).
+__device__ __host__ __forceinline__ Fx fx_from_f32_bits(uint32_t u) {
+  Fx r;
+  fx_zero(r);
+  const uint32_t e = (u >> 23) & 0xffu, frac = u & 0x7fffffu;
+  const uint64_t m = e ? (uint64_t)(frac | 0x800000u) : (uint64_t)frac;
+  if (m == 0) return r;
+  const int sh = (e ? (int)e : 1) - 1;              // 0 .. 253
+  const int limb = sh >> 6, off = sh & 63;
+  r.w[limb] = m << off;
+  if (off > 40 && limb < 4) r.w[limb + 1] = m >> (64 - off);
+  if (u & 0x80000000u) fx_negate(r);
+  return r;
+}
+
+}  // namespace dllm

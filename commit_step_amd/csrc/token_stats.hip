@@ -1,0 +1,723 @@
+// dllm_token_stats: one pass over (B, L, V) logits -> (x0, prob, entropy) per
+// position, optionally followed, in the same launch, by the commit rules.
+//
+// What is computed: mlx-arsenal research note "dLLM block decoding", "What
+// mlx-arsenal ships", token_stats row (proposed token, its probability and the
+// entropy, float32, NaN-safe, greedy or Gumbel-max with an explicit key,
+// suppress_ids removed before the softmax); mojo-dllm "The GPU path", row
+// statistics paragraph (first index of the maximum; p = 1/z; the entropy from
+// sum e^(x-m) and sum e^(x-m)(x-m)).
+//
+// Design for gfx950.  The step reads B*L*V logits once and does a few dozen
+// operations per element, so it is bound by HBM bandwidth, with the vector ALU
+// close behind for bf16; there is no dense contraction and no MFMA.
+//   * Each workgroup streams one row (or a slice of one) with 16-byte loads;
+//     consecutive lanes read consecutive 16 bytes, so every wave load is 1 KiB
+//     contiguous.  The next chunk is loaded while the current one is reduced.
+//   * One pass, where the page's device kernel makes two: the running maximum M
+//     is shared by the 64 lanes of a wave (a DPP max per chunk), so a rise of M
+//     is a rare, wave-uniform event.  Each lane accumulates, relative to M and
+//     in base 2, z- = sum of 2^d over every element except one maximal element,
+//     and S = sum 2^d d, d = (x - M) log2 e.  Keeping the maximal element out of
+//     z- keeps log z = log1p(z-) accurate for peaked rows (z close to 1); it is
+//     excluded exactly once, in the chunk where M rises.
+//   * Wave partials (M, first index of M, z-, S) merge associatively through
+//     LDS; a row split over several workgroups merges its slices through the
+//     caller's workspace, in slice order, so results are bit-reproducible.
+//   * prob = 1 / (1 + z-) (greedy) and H = log1p(z-) - ln2 * S / (1 + z-).
+//   * Rows holding NaN or +inf, or whose unsuppressed logits are all -inf, are
+//     detected after the pass and recomputed by a plain two-pass loop with the
+//     exact limit semantics.
+//   * Fused rules: the workgroup that finishes the last position of a batch row
+//     (a counter in the workspace) runs the ranking rules on the statistics the
+//     launch has just written; the edit rule is decided per position.
+#include <stdarg.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "common.h"
+#include "rules_dev.h"
+
+namespace dllm {
+
+constexpr float kInf = __builtin_inff();
+constexpr int kIdxNone = 0x7fffffff;
+constexpr int kMaxRules = 2;
+
+struct Partial {          // one row slice's statistics (workspace)
+  float M;                // max of the slice (-inf: empty)
+  int idx;                // first index of M
+  float z;                // sum 2^((x-M)log2e) over the slice but one maximal element
+  float S;                // sum 2^d d, d = (x-M)log2e
+  float sb;               // sampled: best score x/T + g
+  int ib;                 // sampled: its index
+  float xb;               // sampled: its logit
+  int pad;
+};
+
+struct StatsArgs {
+  const void *logits;
+  int64_t row_stride;
+  int64_t V;
+  int64_t L;
+  int64_t slice_len;       // elements per slice (multiple of 8)
+  int slices;
+  float inv_temp;
+  uint32_t key0, key1, step;
+  int n_suppress;
+  int first_allowed;       // lowest id not suppressed
+  int32_t suppress[DLLM_MAX_SUPPRESS];   // sorted ascending
+  int32_t *x0;
+  float *prob;
+  float *entropy;
+  // fused rules
+  int n_rank_rules;
+  RuleDev rank_rules[kMaxRules];
+  int has_edit;
+  const uint8_t *edit_mask;
+  uint8_t *edit_out;
+  const int32_t *edit_tokens;
+  double edit_tau;
+  // workspace
+  uint32_t *batch_count;   // [B]
+  uint32_t *row_count;     // [B*L] (slices > 1)
+  Partial *partials;       // [B*L*slices] (slices > 1)
+};
+
+template <typename T> struct ElemT;
+template <> struct ElemT<uint16_t> {   // bf16 bit patterns
+  static constexpr int VEC = 8;        // elements per 16-byte load
+  static constexpr int U = 4;          // loads per lane per chunk
+  __device__ static float at(const uint4 &v, int e) {
+    const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
+    return (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
+  }
+  __device__ static float load1(const uint16_t *p) { return __uint_as_float((uint32_t)*p << 16); }
+};
+template <> struct ElemT<float> {
+  static constexpr int VEC = 4;
+  static constexpr int U = 8;
+  __device__ static float at(const uint4 &v, int e) {
+    const uint32_t w = e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
+    return __uint_as_float(w);
+  }
+  __device__ static float load1(const float *p) { return *p; }
+};
+
+// Wave-local running state.
+struct WaveState {
+  float M;       // wave-uniform running max
+  int idx;       // wave-uniform first index of M
+  float zx, Sx;  // wave-uniform: demoted maxima and ties of M, relative to M
+  float z, S;    // per lane, relative to M
+  float sb;      // per lane sampled best
+  int ib;
+  float xb;
+};
+
+__device__ __forceinline__ float clamp_d(float d) {
+  // d <= 0 always; below -200 (and -inf) the term 2^d is 0 in float32.  An
+  // unsigned min on the bits maps every such d (and -inf) to -200 while leaving
+  // [-200, +0] untouched, so 0 * -inf never arises.  NaN d passes through.
+  return __uint_as_float(min(__float_as_uint(d), 0xC3480000u));
+}
+
+// Process one chunk of CH elements (x[], with element indices given by idx_of).
+template <int CH, typename IdxF>
+__device__ __forceinline__ void chunk_update(WaveState &st, const float (&x)[CH], IdxF idx_of) {
+  float cm = x[0];
+#pragma unroll
+  for (int e = 1; e < CH; ++e) cm = fmaxf(cm, x[e]);
+  const float cmw = wave_max(cm);
+  if (cmw > st.M) {
+    // The wave maximum rises (rare after the first chunks): rescale, demote the
+    // old maximal element into the uniform extra sum, and exclude exactly one
+    // new maximal element from z.
+    if (st.M != -kInf) {
+      const float delta = (st.M - cmw) * kLog2e;
+      const float f = __builtin_amdgcn_exp2f(delta);
+      st.S = f * fmaf(delta, st.z, st.S);
+      st.z = st.z * f;
+      const float zx1 = st.zx + 1.0f;
+      st.Sx = f * fmaf(delta, zx1, st.Sx);
+      st.zx = zx1 * f;
+    }
+    st.M = cmw;
+    int cnt = 0, first = kIdxNone;
+#pragma unroll
+    for (int e = 0; e < CH; ++e) {
+      const bool eq = x[e] == cmw;
+      const float d = clamp_d((x[e] - cmw) * kLog2e);
+      const float t = eq ? 0.0f : __builtin_amdgcn_exp2f(d);
+      st.z += t;
+      st.S = fmaf(t, d, st.S);
+      cnt += eq ? 1 : 0;
+      first = (eq && first == kIdxNone) ? idx_of(e) : first;
+    }
+    const int cnt_w = wave_sum_i(cnt);
+    st.idx = wave_min_i(first);
+    st.zx += (float)(cnt_w - 1);
+  } else if (st.M != -kInf) {
+    const float m = st.M;
+#pragma unroll
+    for (int e = 0; e < CH; ++e) {
+      const float d = clamp_d((x[e] - m) * kLog2e);
+      const float t = __builtin_amdgcn_exp2f(d);
+      st.z += t;
+      st.S = fmaf(t, d, st.S);
+    }
+  }
+}
+
+// Merge partial b into a (a, b relative to their own maxima).
+__device__ __forceinline__ void merge_partial(Partial &a, const Partial &b) {
+  if (b.M == -kInf) return;
+  if (a.M == -kInf) {
+    const float sb = a.sb; const int ib = a.ib; const float xb = a.xb;
+    a = b;
+    // sampling fields merge separately below
+    a.sb = sb; a.ib = ib; a.xb = xb;
+  } else {
+    Partial w = a, o = b;
+    if (b.M > a.M || (b.M == a.M && b.idx < a.idx)) { w = b; o = a; }
+    const float delta = (o.M - w.M) * kLog2e;
+    const float f = __builtin_amdgcn_exp2f(delta);
+    const float zo = 1.0f + o.z;
+    const float z = w.z + zo * f;
+    const float S = w.S + f * fmaf(delta, zo, o.S);
+    const float sb = a.sb; const int ib = a.ib; const float xb = a.xb;
+    a = w;
+    a.z = z;
+    a.S = S;
+    a.sb = sb; a.ib = ib; a.xb = xb;
+  }
+}
+__device__ __forceinline__ void merge_sample(Partial &a, const Partial &b) {
+  if (b.sb > a.sb || (b.sb == a.sb && b.ib < a.ib)) { a.sb = b.sb; a.ib = b.ib; a.xb = b.xb; }
+}
+
+__device__ __forceinline__ bool is_suppressed(const StatsArgs &a, int64_t v) {
+  for (int i = 0; i < a.n_suppress; ++i)
+    if (a.suppress[i] == v) return true;
+  return false;
+}
+
+__device__ __forceinline__ float gumbel_at(const StatsArgs &a, uint32_t b, uint32_t l, int64_t v) {
+  const Philox4 p = philox4x32_10((uint32_t)(v >> 2), l, b, a.step, a.key0, a.key1);
+  return gumbel_from_word(p.w[v & 3]);
+}
+
+// Stream [lo, hi) of one row.  VECLOAD: 16-byte loads (row start 16-byte
+// aligned, lo/hi multiples of VEC).  Returns this workgroup's partial in
+// *out (valid in thread 0).
+template <typename T, int NT, bool SAMPLE, bool VECLOAD>
+__device__ void stream_slice(const StatsArgs &a, const T *row, int64_t lo, int64_t hi,
+                             uint32_t b, uint32_t l, Partial *wave_parts, Partial *out) {
+  using E = ElemT<T>;
+  constexpr int VEC = VECLOAD ? E::VEC : 1;
+  constexpr int U = VECLOAD ? E::U : 8;
+  constexpr int CH = VEC * U;
+  constexpr int STEP = NT * CH;                 // elements per workgroup iteration
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  WaveState st;
+  st.M = -kInf; st.idx = kIdxNone; st.zx = 0.f; st.Sx = 0.f; st.z = 0.f; st.S = 0.f;
+  st.sb = -kInf; st.ib = kIdxNone; st.xb = -kInf;
+
+  int sp = 0;   // next suppress id not below the current iteration
+  for (int64_t base = lo; base < hi; base += STEP) {
+    float x[CH];
+    if constexpr (VECLOAD) {
+      uint4 raw[U];
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        const int64_t v0 = base + (int64_t)(k * NT + tid) * VEC;
+        if (v0 < hi) raw[k] = *reinterpret_cast<const uint4 *>(row + v0);
+        else raw[k] = make_uint4(0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u);
+      }
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        const int64_t v0 = base + (int64_t)(k * NT + tid) * VEC;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+          x[k * VEC + e] = (v0 < hi) ? E::at(raw[k], e) : -kInf;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        const int64_t v = base + (int64_t)(k * NT + tid);
+        x[k] = (v < hi) ? E::load1(row + v) : -kInf;
+      }
+    }
+    // suppress ids inside this iteration (rare, workgroup-uniform test)
+    while (sp < a.n_suppress && a.suppress[sp] < base) ++sp;
+    if (sp < a.n_suppress && a.suppress[sp] < base + STEP) {
+      for (int q = sp; q < a.n_suppress && a.suppress[q] < base + STEP; ++q) {
+        const int64_t s = a.suppress[q];
+#pragma unroll
+        for (int k = 0; k < U; ++k) {
+          const int64_t v0 = base + (int64_t)(k * NT + tid) * VEC;
+#pragma unroll
+          for (int e = 0; e < VEC; ++e)
+            if (v0 + e == s) x[k * VEC + e] = -kInf;
+        }
+      }
+    }
+    auto idx_of = [&](int e) -> int {
+      return (int)(base + (int64_t)((e / VEC) * NT + tid) * VEC + (e % VEC));
+    };
+    if constexpr (SAMPLE) {
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        const int64_t v0 = base + (int64_t)(k * NT + tid) * VEC;
+        if constexpr (VEC >= 4) {
+#pragma unroll
+          for (int q = 0; q < VEC / 4; ++q) {
+            const int64_t vq = v0 + 4 * q;
+            const Philox4 p = philox4x32_10((uint32_t)(vq >> 2), l, b, a.step, a.key0, a.key1);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              const float xv = x[k * VEC + 4 * q + j];
+              const float s = fmaf(xv, a.inv_temp, gumbel_from_word(p.w[j]));
+              if (s > st.sb) { st.sb = s; st.ib = (int)(vq + j); st.xb = xv; }
+            }
+          }
+        } else {
+          const float xv = x[k];
+          if (v0 < hi) {
+            const float s = fmaf(xv, a.inv_temp, gumbel_at(a, b, l, v0));
+            if (s > st.sb) { st.sb = s; st.ib = (int)v0; st.xb = xv; }
+          }
+        }
+      }
+    }
+    chunk_update<CH>(st, x, idx_of);
+  }
+
+  // Wave partial -> LDS.
+  Partial p;
+  p.M = st.M;
+  p.idx = st.idx;
+  p.z = wave_sum(st.z) + st.zx;
+  p.S = wave_sum(st.S) + st.Sx;
+  p.sb = -kInf; p.ib = kIdxNone; p.xb = -kInf; p.pad = 0;
+  if constexpr (SAMPLE) {
+    // first-best over the lanes: max score, lowest index on ties
+    float sb = st.sb; int ib = st.ib; float xb = st.xb;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float osb = __shfl_xor(sb, off);
+      const int oib = __shfl_xor(ib, off);
+      const float oxb = __shfl_xor(xb, off);
+      if (osb > sb || (osb == sb && oib < ib)) { sb = osb; ib = oib; xb = oxb; }
+    }
+    p.sb = sb; p.ib = ib; p.xb = xb;
+  }
+  if (lane == 0) wave_parts[wave] = p;
+  __syncthreads();
+  if (tid == 0) {
+    Partial acc = wave_parts[0];
+    for (int w = 1; w < NT / 64; ++w) {
+      merge_partial(acc, wave_parts[w]);
+      if constexpr (SAMPLE) merge_sample(acc, wave_parts[w]);
+    }
+    *out = acc;
+  }
+}
+
+struct RowResult { int x0; float prob; float ent; };
+
+// Plain two-pass recomputation of a degenerate row (NaN, +inf, or no finite
+// unsuppressed logit), with the limit semantics of the header.  Every thread
+// of the workgroup calls it; the result is valid in thread 0.
+template <typename T, int NT, bool SAMPLE>
+__device__ RowResult slow_row(const StatsArgs &a, const T *row, uint32_t b, uint32_t l,
+                              unsigned char *scratch) {
+  using E = ElemT<T>;
+  const int tid = threadIdx.x;
+  float *fs = reinterpret_cast<float *>(scratch);          // [NT]
+  int *is = reinterpret_cast<int *>(scratch) + NT;         // [NT]
+  int *js = reinterpret_cast<int *>(scratch) + 2 * NT;     // [NT]
+  float *gs = reinterpret_cast<float *>(scratch) + 3 * NT; // [NT]
+  const int64_t V = a.V;
+  // pass 1: max (NaN -> -inf), its first index, number and first index of +inf
+  float m = -kInf; int im = kIdxNone; int ninf = 0; int iinf = kIdxNone;
+  for (int64_t v = tid; v < V; v += NT) {
+    if (is_suppressed(a, v)) continue;
+    float x = E::load1(row + v);
+    if (x != x) x = -kInf;
+    if (x > m) { m = x; im = (int)v; }
+    if (x == kInf) { ++ninf; if (iinf == kIdxNone) iinf = (int)v; }
+  }
+  fs[tid] = m; is[tid] = im; js[tid] = ninf; gs[tid] = __int_as_float(iinf);
+  __syncthreads();
+  __shared__ float s_m;
+  __shared__ int s_im, s_ninf, s_iinf;
+  if (tid == 0) {
+    float M = -kInf; int IM = kIdxNone; int N = 0; int II = kIdxNone;
+    for (int t = 0; t < NT; ++t) {
+      if (fs[t] > M || (fs[t] == M && is[t] < IM)) { M = fs[t]; IM = is[t]; }
+      N += js[t];
+      II = min(II, __float_as_int(gs[t]));
+    }
+    s_m = M; s_im = IM; s_ninf = N; s_iinf = II;
+  }
+  __syncthreads();
+  const float M = s_m;
+  const int nA = (int)V - a.n_suppress;
+  const bool finite = bits_finite(__float_as_uint(M));
+  // pass 2: sums relative to M excluding the first maximal element (finite M),
+  // and the sampled argmax over the relevant support.
+  float z = 0.f, S = 0.f, sb = -kInf, xb = -kInf; int ib = kIdxNone;
+  for (int64_t v = tid; v < V; v += NT) {
+    if (is_suppressed(a, v)) continue;
+    float x = E::load1(row + v);
+    if (x != x) x = -kInf;
+    if (finite) {
+      if (v != s_im) {
+        const float d = (x - M) * kLog2e;
+        const float t = __builtin_amdgcn_exp2f(d);
+        z += t;
+        if (t > 0.f) S = fmaf(t, d, S);
+      }
+      if (SAMPLE) {
+        const float s = fmaf(x, a.inv_temp, gumbel_at(a, b, l, v));
+        if (s > sb) { sb = s; ib = (int)v; xb = x; }
+      }
+    } else if (SAMPLE) {
+      const bool in_support = (M == -kInf) ? true : (x == kInf);
+      if (in_support) {
+        const float g = gumbel_at(a, b, l, v);
+        if (g > sb) { sb = g; ib = (int)v; xb = x; }
+      }
+    }
+  }
+  __syncthreads();
+  fs[tid] = z; gs[tid] = S; is[tid] = ib; js[tid] = __float_as_int(sb);
+  float *xs = reinterpret_cast<float *>(scratch) + 4 * NT;
+  xs[tid] = xb;
+  __syncthreads();
+  RowResult r;
+  r.x0 = 0; r.prob = 0.f; r.ent = 0.f;
+  if (tid == 0) {
+    float Z = 0.f, SS = 0.f, SB = -kInf, XB = -kInf; int IB = kIdxNone;
+    for (int t = 0; t < NT; ++t) {
+      Z += fs[t];
+      SS += gs[t];
+      const float s = __int_as_float(js[t]);
+      if (s > SB || (s == SB && is[t] < IB)) { SB = s; IB = is[t]; XB = xs[t]; }
+    }
+    if (finite) {
+      r.ent = log1pf(Z) - kLn2 * SS / (1.0f + Z);
+      if (SAMPLE) {
+        r.x0 = IB;
+        r.prob = __builtin_amdgcn_exp2f((XB - M) * kLog2e) / (1.0f + Z);
+      } else {
+        r.x0 = s_im;
+        r.prob = 1.0f / (1.0f + Z);
+      }
+    } else if (M == -kInf) {
+      r.x0 = SAMPLE ? IB : a.first_allowed;
+      r.prob = 1.0f / (float)nA;
+      r.ent = logf((float)nA);
+    } else {
+      r.x0 = SAMPLE ? IB : s_iinf;
+      r.prob = 1.0f / (float)s_ninf;
+      r.ent = logf((float)s_ninf);
+    }
+  }
+  return r;
+}
+
+template <typename T, int NT, bool SAMPLE, bool VECLOAD>
+__global__ __launch_bounds__(NT) void token_stats_kernel(StatsArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];   // rules (dynamic)
+  __shared__ Partial wave_parts[NT / 64];
+  __shared__ Partial slice_parts_acc;
+  __shared__ int s_flag;
+  __shared__ __align__(16) unsigned char slow_scratch[5 * NT * 4];
+
+  const int tid = threadIdx.x;
+  const int64_t wg = blockIdx.x;
+  const int64_t row_id = wg / a.slices;
+  const int slice = (int)(wg - row_id * a.slices);
+  const uint32_t b = (uint32_t)(row_id / a.L), l = (uint32_t)(row_id - (int64_t)b * a.L);
+  const T *row = reinterpret_cast<const T *>(a.logits) + row_id * a.row_stride;
+  const int64_t lo = (int64_t)slice * a.slice_len;
+  const int64_t hi = min(lo + a.slice_len, a.V);
+
+  stream_slice<T, NT, SAMPLE, VECLOAD>(a, row, lo, hi, b, l, wave_parts, &slice_parts_acc);
+
+  // Split rows: publish the slice partial; the last slice to finish merges.
+  if (a.slices > 1) {
+    if (tid == 0) {
+      a.partials[row_id * a.slices + slice] = slice_parts_acc;
+      __threadfence();
+      const uint32_t prev = atomicAdd(&a.row_count[row_id], 1u);
+      s_flag = (prev == (uint32_t)(a.slices - 1));
+      if (s_flag) {
+        __threadfence();
+        Partial acc = a.partials[row_id * a.slices];
+        for (int s = 1; s < a.slices; ++s) {
+          const Partial q = a.partials[row_id * a.slices + s];
+          merge_partial(acc, q);
+          if (SAMPLE) merge_sample(acc, q);
+        }
+        slice_parts_acc = acc;
+        a.row_count[row_id] = 0u;       // leave the workspace zeroed
+      }
+    }
+    __syncthreads();
+    if (!s_flag) return;
+  }
+
+  // Finalize the row.
+  __shared__ int s_slow;
+  RowResult res;
+  res.x0 = 0; res.prob = 0.f; res.ent = 0.f;
+  if (tid == 0) {
+    const Partial p = slice_parts_acc;
+    const bool ok = bits_finite(__float_as_uint(p.M)) && bits_finite(__float_as_uint(p.z)) &&
+                    bits_finite(__float_as_uint(p.S)) &&
+                    (!SAMPLE || (p.ib != kIdxNone && bits_finite(__float_as_uint(p.sb))));
+    s_slow = !ok;
+    if (ok) {
+      const float zf = 1.0f + p.z;
+      res.ent = log1pf(p.z) - kLn2 * p.S / zf;
+      if (SAMPLE) {
+        res.x0 = p.ib;
+        res.prob = __builtin_amdgcn_exp2f((p.xb - p.M) * kLog2e) / zf;
+      } else {
+        res.x0 = p.idx;
+        res.prob = 1.0f / zf;
+      }
+    }
+  }
+  __syncthreads();
+  if (s_slow) res = slow_row<T, NT, SAMPLE>(a, row, b, l, slow_scratch);
+
+  if (tid == 0) {
+    a.x0[row_id] = res.x0;
+    a.prob[row_id] = res.prob;
+    a.entropy[row_id] = res.ent;
+    if (a.has_edit)
+      a.edit_out[row_id] = edit_decision(a.edit_mask[row_id], res.x0, a.edit_tokens[row_id],
+                                         res.prob, a.edit_tau);
+  }
+  if (a.n_rank_rules == 0) return;
+
+  // Batch-row rules: the workgroup that completes the batch row runs them.
+  if (tid == 0) {
+    __threadfence();
+    const uint32_t prev = atomicAdd(&a.batch_count[b], 1u);
+    s_flag = (prev == (uint32_t)(a.L - 1));
+    if (s_flag) __threadfence();
+  }
+  __syncthreads();
+  if (!s_flag) return;
+  __threadfence();
+  for (int r = 0; r < a.n_rank_rules; ++r)
+    run_batch_rule(a.rank_rules[r], (int)b, (int)a.L, a.prob, a.entropy, smem);
+  if (tid == 0) a.batch_count[b] = 0u;   // leave the workspace zeroed
+}
+
+// ---------------------------------------------------------------- host side
+
+namespace {
+
+struct Plan {
+  int nt;
+  int slices;
+  int64_t slice_len;
+  bool vec;
+};
+
+Plan make_plan(int dtype, int64_t rows, int64_t V, int64_t row_stride, const void *logits) {
+  const int esz = dtype == DLLM_BF16 ? 2 : 4;
+  const int vecn = 16 / esz;
+  Plan p;
+  p.vec = ((uintptr_t)logits % 16 == 0) && ((row_stride * esz) % 16 == 0) && (V % vecn == 0);
+  const int cus = device_cu_count();
+  // Enough waves to cover HBM latency: aim for >= 16 waves per CU.
+  if (rows >= 4LL * cus || V < 16384) p.nt = 256;
+  else p.nt = 1024;
+  p.slices = 1;
+  const int64_t wgs = rows;
+  if (wgs < cus && V >= 8192) {
+    int64_t s = (cus + rows - 1) / rows;
+    const int64_t min_slice = 4096;               // keep slices worth a launch
+    s = std::min<int64_t>(s, std::max<int64_t>(1, V / min_slice));
+    p.slices = (int)std::max<int64_t>(1, s);
+  }
+  int64_t sl = (V + p.slices - 1) / p.slices;
+  sl = (sl + 7) / 8 * 8;
+  p.slice_len = sl;
+  p.slices = (int)((V + sl - 1) / sl);
+  return p;
+}
+
+size_t workspace_bytes_for(int64_t B, int64_t L, int slices) {
+  size_t bytes = ((size_t)B * 4 + 255) / 256 * 256;
+  if (slices > 1) {
+    bytes += ((size_t)B * L * 4 + 255) / 256 * 256;
+    bytes += (size_t)B * L * slices * sizeof(Partial);
+  }
+  return bytes;
+}
+
+template <typename T, int NT>
+hipError_t launch_t(const Plan &p, const StatsArgs &a, int64_t rows, bool sample, size_t smem,
+                    hipStream_t s) {
+  dim3 grid((unsigned)(rows * p.slices)), block(NT);
+  if (sample) {
+    if (p.vec) token_stats_kernel<T, NT, true, true><<<grid, block, smem, s>>>(a);
+    else token_stats_kernel<T, NT, true, false><<<grid, block, smem, s>>>(a);
+  } else {
+    if (p.vec) token_stats_kernel<T, NT, false, true><<<grid, block, smem, s>>>(a);
+    else token_stats_kernel<T, NT, false, false><<<grid, block, smem, s>>>(a);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Host helper shared with the transfer entry points: validates a rule and
+// fills its device view.
+int prepare_rule(const dllm_rule &r, RuleDev &d, int64_t B, int64_t L, const char *who);
+
+}  // namespace dllm
+
+using namespace dllm;
+
+extern "C" size_t dllm_token_stats_workspace_size(int dtype, int64_t B, int64_t L, int64_t V) {
+  if ((dtype != DLLM_F32 && dtype != DLLM_BF16) || B < 0 || L < 0 || V < 1) return 0;
+  const Plan p = make_plan(dtype, B * L, V, V, nullptr);
+  return workspace_bytes_for(B, L, p.slices);
+}
+
+extern "C" int dllm_token_stats(const void *logits, int dtype, int64_t B, int64_t L, int64_t V,
+                                int64_t row_stride, float temperature, uint64_t seed,
+                                uint64_t step, const int32_t *suppress_ids, int n_suppress,
+                                int32_t *x0, float *prob, float *entropy,
+                                const dllm_rule *rules, int n_rules, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  if (dtype != DLLM_F32 && dtype != DLLM_BF16)
+    return fail(DLLM_ERR_DTYPE, "dllm_token_stats: dtype %d is neither DLLM_F32 nor DLLM_BF16", dtype);
+  if (B < 0 || L < 0) return fail(DLLM_ERR_ARG, "dllm_token_stats: B and L must be >= 0");
+  if (V < 1 || V > 0x7fffffffLL)
+    return fail(DLLM_ERR_ARG, "dllm_token_stats: V = %lld must be in [1, 2^31)", (long long)V);
+  if (row_stride < V) return fail(DLLM_ERR_ARG, "dllm_token_stats: row_stride < V");
+  if (!(temperature >= 0.0f) || temperature == __builtin_inff())
+    return fail(DLLM_ERR_ARG, "dllm_token_stats: temperature must be finite and >= 0");
+  if (step > 0xffffffffull) return fail(DLLM_ERR_ARG, "dllm_token_stats: step must be < 2^32");
+  if (n_suppress < 0 || n_suppress > DLLM_MAX_SUPPRESS)
+    return fail(DLLM_ERR_ARG, "dllm_token_stats: n_suppress must be in [0, %d]", DLLM_MAX_SUPPRESS);
+  if (n_suppress > 0 && !suppress_ids)
+    return fail(DLLM_ERR_ARG, "dllm_token_stats: suppress_ids is NULL");
+  if (n_rules < 0 || n_rules > kMaxRules || (n_rules > 0 && !rules))
+    return fail(DLLM_ERR_ARG, "dllm_token_stats: n_rules must be 0..%d with a rules array", kMaxRules);
+  if (B == 0 || L == 0) return ok();
+  if (!logits || !x0 || !prob || !entropy)
+    return fail(DLLM_ERR_ARG, "dllm_token_stats: logits, x0, prob and entropy must be non-NULL");
+
+  StatsArgs a;
+  memset(&a, 0, sizeof(a));
+  // suppress ids: sorted, distinct, in range, not every id
+  for (int i = 0; i < n_suppress; ++i) {
+    const int32_t s = suppress_ids[i];
+    if (s < 0 || s >= V)
+      return fail(DLLM_ERR_ARG, "dllm_token_stats: suppress id %d is outside [0, V)", s);
+    int j = i;
+    while (j > 0 && a.suppress[j - 1] > s) { a.suppress[j] = a.suppress[j - 1]; --j; }
+    a.suppress[j] = s;
+  }
+  for (int i = 1; i < n_suppress; ++i)
+    if (a.suppress[i] == a.suppress[i - 1])
+      return fail(DLLM_ERR_ARG, "dllm_token_stats: suppress id %d appears twice", a.suppress[i]);
+  if (n_suppress >= V) return fail(DLLM_ERR_ARG, "dllm_token_stats: every id is suppressed");
+  int first_allowed = 0;
+  for (int i = 0; i < n_suppress && a.suppress[i] == first_allowed; ++i) ++first_allowed;
+
+  // rules
+  bool seen[6] = {false, false, false, false, false, false};
+  const void *outs[kMaxRules] = {nullptr, nullptr};
+  for (int i = 0; i < n_rules; ++i) {
+    const dllm_rule &r = rules[i];
+    if (r.kind < DLLM_RULE_THRESHOLD || r.kind > DLLM_RULE_EDIT)
+      return fail(DLLM_ERR_ARG, "dllm_token_stats: rules[%d].kind = %d is not a DLLM_RULE_*", i, r.kind);
+    if (seen[r.kind]) return fail(DLLM_ERR_ARG, "dllm_token_stats: rule kind %d appears twice", r.kind);
+    seen[r.kind] = true;
+    outs[i] = r.out;
+    if (r.out == (const void *)x0 || r.out == (const void *)prob || r.out == (const void *)entropy ||
+        r.out == (const void *)r.mask || r.out == (const void *)logits)
+      return fail(DLLM_ERR_ARG, "dllm_token_stats: rules[%d].out aliases another array", i);
+    if (r.kind == DLLM_RULE_EDIT) {
+      if (!r.mask || !r.out || !r.tokens)
+        return fail(DLLM_ERR_ARG, "dllm_token_stats: edit rule needs mask, out and tokens");
+      if (r.param != r.param) return fail(DLLM_ERR_ARG, "dllm_token_stats: tau_edit is NaN");
+      a.has_edit = 1;
+      a.edit_mask = r.mask;
+      a.edit_out = r.out;
+      a.edit_tokens = r.tokens;
+      a.edit_tau = r.param;
+    } else {
+      if (L > DLLM_MAX_L)
+        return fail(DLLM_ERR_UNSUPPORTED, "dllm_token_stats: L = %lld exceeds DLLM_MAX_L = %d",
+                    (long long)L, DLLM_MAX_L);
+      const int rc = prepare_rule(r, a.rank_rules[a.n_rank_rules], B, L, "dllm_token_stats");
+      if (rc != DLLM_OK) return rc;
+      ++a.n_rank_rules;
+    }
+  }
+  if (n_rules == 2 && outs[0] == outs[1])
+    return fail(DLLM_ERR_ARG, "dllm_token_stats: the two rules share an output");
+
+  const int64_t rows = B * L;
+  const Plan p = make_plan(dtype, rows, V, row_stride, logits);
+  const size_t need = workspace_bytes_for(B, L, p.slices);
+  if (!workspace) return fail(DLLM_ERR_ARG, "dllm_token_stats: workspace is NULL");
+  if (workspace_bytes < need)
+    return fail(DLLM_ERR_SHAPE, "dllm_token_stats: workspace has %zu bytes, this shape needs %zu",
+                workspace_bytes, need);
+  if ((uintptr_t)workspace % 16)
+    return fail(DLLM_ERR_ARG, "dllm_token_stats: workspace must be 16-byte aligned");
+
+  unsigned char *ws = static_cast<unsigned char *>(workspace);
+  a.batch_count = reinterpret_cast<uint32_t *>(ws);
+  size_t off = ((size_t)B * 4 + 255) / 256 * 256;
+  if (p.slices > 1) {
+    a.row_count = reinterpret_cast<uint32_t *>(ws + off);
+    off += ((size_t)rows * 4 + 255) / 256 * 256;
+    a.partials = reinterpret_cast<Partial *>(ws + off);
+  }
+  a.logits = logits;
+  a.row_stride = row_stride;
+  a.V = V;
+  a.L = L;
+  a.slice_len = p.slice_len;
+  a.slices = p.slices;
+  a.inv_temp = temperature > 0.0f ? 1.0f / temperature : 0.0f;
+  a.key0 = (uint32_t)(seed & 0xffffffffu);
+  a.key1 = (uint32_t)(seed >> 32);
+  a.step = (uint32_t)step;
+  a.n_suppress = n_suppress;
+  a.first_allowed = first_allowed;
+  a.x0 = x0;
+  a.prob = prob;
+  a.entropy = entropy;
+
+  const bool sample = temperature > 0.0f;
+  const size_t smem = a.n_rank_rules ? rule_smem_bytes((int)L) : 0;
+  hipError_t e;
+  if (dtype == DLLM_BF16) {
+    e = p.nt == 1024 ? launch_t<uint16_t, 1024>(p, a, rows, sample, smem, stream)
+                     : launch_t<uint16_t, 256>(p, a, rows, sample, smem, stream);
+  } else {
+    e = p.nt == 1024 ? launch_t<float, 1024>(p, a, rows, sample, smem, stream)
+                     : launch_t<float, 256>(p, a, rows, sample, smem, stream);
+  }
+  if (e != hipSuccess)
+    return fail(DLLM_ERR_HIP, "dllm_token_stats: launch failed: %s", hipGetErrorString(e));
+  return ok();
+}

@@ -1,0 +1,220 @@
+/*
+ * libdllm_commit -- the per-step commit of masked (absorbing-state) diffusion-LM
+ * decoding, for AMD Instinct MI355X (gfx950).
+ *
+ * One decoding step of a masked diffusion LM runs the model over the canvas,
+ * proposes a token for every position, and commits a subset of the proposals
+ * (mlx-arsenal research note "dLLM block decoding", section "The pattern").
+ * This library is that commit: the token statistics of the logits and the
+ * commit rules, as pure functions; the model and the decode loop stay with the
+ * caller (same section: "the loop stays with the caller").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Return value: DLLM_OK (0) or a negative DLLM_ERR_* code.  On error nothing
+ *    is launched and no output is touched; dllm_last_error() returns a message
+ *    naming the offending argument (per calling thread).
+ *  - Memory: every array is caller-owned, contiguous, row-major DEVICE memory,
+ *    except where an argument says HOST.  The library never allocates, frees
+ *    or synchronizes; it keeps no state between calls except the workspace the
+ *    caller passes to dllm_token_stats.
+ *  - Streams: work is enqueued on `stream` (0 = the null stream); results are
+ *    valid once the stream has reached that point.
+ *  - Shapes: B batch rows of L positions; position (b, l) is element b*L + l of
+ *    every (B, L) array.  B = 0 or L = 0 returns DLLM_OK with no launch.
+ *  - Masks are uint8: input masks treat any nonzero byte as true; output masks
+ *    are written as 0 or 1 for every position.
+ *  - Scores are float32.  A NaN score counts as the worst possible score: -inf
+ *    for a confidence, +inf for an entropy.  -0.0 and +0.0 are equal.
+ *  - Rankings are stable: equal scores order by lower position ("Deviations
+ *    from the references": sorting is stable, the forced token is the first
+ *    maximal one).
+ *  - A batch row may hold at most DLLM_MAX_L positions for the ranking rules
+ *    (threshold, topk, factor, entropy_bound); longer rows return
+ *    DLLM_ERR_UNSUPPORTED.
+ */
+#ifndef DLLM_COMMIT_H
+#define DLLM_COMMIT_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  DLLM_OK = 0,
+  DLLM_ERR_ARG = -1,          /* bad pointer, size, parameter or combination  */
+  DLLM_ERR_DTYPE = -2,        /* unknown logits dtype                         */
+  DLLM_ERR_SHAPE = -3,        /* workspace too small for the shape            */
+  DLLM_ERR_HIP = -4,          /* a HIP call or kernel launch failed           */
+  DLLM_ERR_UNSUPPORTED = -5   /* a size beyond what the library implements    */
+};
+
+enum { DLLM_F32 = 0, DLLM_BF16 = 1 };
+
+#define DLLM_MAX_L 4096
+#define DLLM_MAX_SUPPRESS 64
+
+enum {
+  DLLM_RULE_THRESHOLD = 1,
+  DLLM_RULE_TOPK = 2,
+  DLLM_RULE_FACTOR = 3,
+  DLLM_RULE_ENTROPY_BOUND = 4,
+  DLLM_RULE_EDIT = 5
+};
+
+/* One commit rule run inside dllm_token_stats on the statistics it has just
+ * computed (same launch).  The result is identical to calling the matching
+ * dllm_transfer_* function on dllm_token_stats' outputs.
+ *   kind    DLLM_RULE_*.
+ *   mask    (B, L) uint8: the candidates (for EDIT: the editable positions).
+ *   out     (B, L) uint8: the commit mask (for EDIT: the edit mask); must not
+ *           alias any other array of the call.
+ *   param   tau (THRESHOLD), f (FACTOR), gamma (ENTROPY_BOUND), tau_edit (EDIT);
+ *           ignored for TOPK.  Must not be NaN.
+ *   strict  THRESHOLD only: 0 -> conf >= tau, 1 -> conf > tau.
+ *   k       TOPK only: (B,) int32 quotas.
+ *   tokens  EDIT only: (B, L) int32 current canvas.
+ * THRESHOLD / FACTOR / TOPK rank by prob, ENTROPY_BOUND by entropy, EDIT uses
+ * x0, prob and tokens. */
+typedef struct {
+  int kind;
+  const uint8_t *mask;
+  uint8_t *out;
+  double param;
+  int strict;
+  const int32_t *k;
+  const int32_t *tokens;
+} dllm_rule;
+
+/* ---------------------------------------------------------------------------
+ * dllm_token_stats -- per position: the proposed token x0, its probability and
+ * the entropy of the position's distribution (mlx-arsenal "dLLM block
+ * decoding", "What mlx-arsenal ships", token_stats row: float32, NaN-safe,
+ * greedy or Gumbel-max sampling with an explicit key, suppress_ids).
+ *
+ *   logits       (B, L, V) DEVICE, dtype DLLM_F32 or DLLM_BF16; the logits of
+ *                position (b, l) start at element (b*L + l) * row_stride.
+ *   row_stride   elements between consecutive positions, >= V.
+ *   temperature  0 -> greedy: x0 is the first index of the largest logit.
+ *                > 0 -> Gumbel-max: x0 is the first index of the largest
+ *                logit/temperature + g, g = -log(-log u) with u drawn by
+ *                Philox4x32-10 (Salmon et al., SC'11) under key (seed low 32,
+ *                seed high 32) at counter (v/4, l, b, step), word v%4, and
+ *                u = ((word >> 9) + 0.5) * 2^-23.  Must be finite and >= 0.
+ *   seed, step   the noise key and the per-step counter word; step < 2^32.
+ *                Ignored when temperature == 0.
+ *   suppress_ids HOST array of n_suppress distinct ids in [0, V) removed before
+ *                the softmax; n_suppress <= DLLM_MAX_SUPPRESS and < V; may be
+ *                NULL when n_suppress == 0.
+ *   x0           (B, L) int32 DEVICE output.
+ *   prob         (B, L) float32 DEVICE output: softmax(logits)[x0], untempered.
+ *   entropy      (B, L) float32 DEVICE output: -sum p log p of softmax(logits)
+ *                over the unsuppressed ids (natural log), untempered.
+ *   rules        HOST array of n_rules (0..2) rules fused into the same launch,
+ *                or NULL.  At most one rule of each kind.
+ *   workspace    DEVICE scratch of at least dllm_token_stats_workspace_size()
+ *                bytes for this shape, zero-filled by the caller before its
+ *                first use; every successful call leaves it zero-filled again,
+ *                so it can be reused by later calls on the same stream.  Two
+ *                calls in flight at once must not share a workspace.
+ *
+ * NaN safety: a NaN logit counts as -inf.  A position whose unsuppressed
+ * logits are all -inf is uniform over the unsuppressed ids; a position with
+ * +inf logits is uniform over its +inf ids.  No output is ever NaN.
+ * -------------------------------------------------------------------------*/
+int dllm_token_stats(const void *logits, int dtype, int64_t B, int64_t L,
+                     int64_t V, int64_t row_stride, float temperature,
+                     uint64_t seed, uint64_t step,
+                     const int32_t *suppress_ids, int n_suppress,
+                     int32_t *x0, float *prob, float *entropy,
+                     const dllm_rule *rules, int n_rules,
+                     void *workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
+/* Bytes of workspace dllm_token_stats needs for this shape on the current
+ * device (a pure function of the arguments and the device).  Returns 0 on bad
+ * arguments. */
+size_t dllm_token_stats_workspace_size(int dtype, int64_t B, int64_t L,
+                                       int64_t V);
+
+/* threshold_transfer ("What mlx-arsenal ships", threshold_transfer row; mlxcel
+ * "Block Diffusion", "LLaDA-2 Block Unmasking"): per batch row, commit every
+ * candidate with conf >= tau (conf > tau when strict != 0); if no candidate
+ * passes, commit exactly one, the first candidate of maximal confidence.
+ * conf (B, L) float32, cand (B, L) uint8, commit (B, L) uint8 out.  tau not NaN. */
+int dllm_transfer_threshold(const float *conf, const uint8_t *cand, int64_t B,
+                            int64_t L, double tau, int strict, uint8_t *commit,
+                            hipStream_t stream);
+
+/* topk_transfer (topk_transfer row; mojo-dllm "The loop LLaDA uses"): commit
+ * the k[b] most confident candidates of batch row b.  k (B,) int32 DEVICE;
+ * k[b] <= 0 commits nothing, k[b] >= #candidates commits all of them. */
+int dllm_transfer_topk(const float *conf, const uint8_t *cand, const int32_t *k,
+                       int64_t B, int64_t L, uint8_t *commit,
+                       hipStream_t stream);
+
+/* factor_transfer (factor_transfer row; "Deviations": no off-by-one): sort the
+ * candidates by decreasing confidence c_(0) >= c_(1) >= ...; commit the longest
+ * prefix on which (i + 1) * (1 - c_(i)) <= f, evaluated exactly, and at least
+ * one candidate.  f not NaN. */
+int dllm_transfer_factor(const float *conf, const uint8_t *cand, int64_t B,
+                         int64_t L, double f, uint8_t *commit,
+                         hipStream_t stream);
+
+/* entropy_bound_transfer (entropy_bound_transfer row; mlxcel "Samplers and
+ * Reveal Policies": at least one accepted): sort the candidates by increasing
+ * entropy H_(0) <= H_(1) <= ...; commit the longest prefix on which the
+ * exclusive sum sum_{j<i} H_(j) <= gamma, evaluated exactly, and at least one
+ * candidate.  gamma not NaN. */
+int dllm_transfer_entropy_bound(const float *entropy, const uint8_t *cand,
+                                int64_t B, int64_t L, double gamma,
+                                uint8_t *commit, hipStream_t stream);
+
+/* edit_transfer (edit_transfer row; "Token editing (LLaDA2.1)"): edit[b, l] =
+ * editable[b, l] && x0[b, l] != tokens[b, l] && prob[b, l] > tau_edit (strict;
+ * nothing is forced).  tau_edit not NaN. */
+int dllm_transfer_edit(const int32_t *x0, const float *prob,
+                       const int32_t *tokens, const uint8_t *editable,
+                       int64_t B, int64_t L, double tau_edit, uint8_t *edit,
+                       hipStream_t stream);
+
+/* transfer_schedule (transfer_schedule row; mojo-dllm "The loop LLaDA uses":
+ * masked positions spread over the steps evenly): schedule[b, s] =
+ * n/steps + (s < n % steps ? 1 : 0) with n = max(n_masked[b], 0).
+ * n_masked (B,) int32 DEVICE, schedule (B, steps) int32 DEVICE out, steps >= 1. */
+int dllm_transfer_schedule(const int32_t *n_masked, int64_t B, int32_t steps,
+                           int32_t *schedule, hipStream_t stream);
+
+/* block_ranges (block_ranges row: prompt-relative or absolute-aligned; the
+ * aligned loop of "Token editing (LLaDA2.1)"): the [start, end) blocks covering
+ * the generation region [prompt_len, prompt_len + gen_len).  align == 0: blocks
+ * start at prompt_len; align != 0: blocks are aligned on multiples of
+ * block_len, the first one starting at floor(prompt_len / block_len) *
+ * block_len.  The last block ends at prompt_len + gen_len; gen_len == 0 gives
+ * no block.  HOST only.  Writes min(count, cap) pairs to out[2i], out[2i+1]
+ * (out may be NULL when cap == 0) and returns the number of blocks, or a
+ * negative DLLM_ERR_* code. */
+int64_t dllm_block_ranges(int64_t prompt_len, int64_t gen_len,
+                          int64_t block_len, int align, int64_t *out,
+                          int64_t cap);
+
+/* block_causal_mask (mlx_arsenal.attention.block_causal_mask: bidirectional
+ * inside a block, causal across blocks, aligned on absolute positions;
+ * "Mask conventions": additive, 0 attend, -inf blocked): out[q, k] = 0.0f if
+ * k / block_len <= q / block_len, else -inf.  out (L, L) float32 DEVICE. */
+int dllm_block_causal_mask(int64_t L, int64_t block_len, float *out,
+                           hipStream_t stream);
+
+/* Message describing the last error returned on the calling thread ("" if
+ * none). */
+const char *dllm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DLLM_COMMIT_H */

@@ -1,0 +1,132 @@
+"""The C-ABI library loads and exports what include/dllm_commit.h declares;
+host-only logic (block_ranges, argument validation) is checked on the CPU.
+No kernel is launched here."""
+import ctypes
+import glob
+import math
+import os
+import re
+from itertools import product
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import commit_step_amd
+    path = commit_step_amd.library_path()
+    if not os.path.exists(path):
+        from commit_step_amd.build import build
+        build(verbose=False)
+    return commit_step_amd.load_library()
+
+
+def _declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names.update(re.findall(r"\b(dllm_\w+)\s*\(", text))
+    return sorted(names)
+
+
+def test_header_declares_the_entry_points():
+    names = _declared_functions()
+    for n in ["dllm_token_stats", "dllm_transfer_threshold", "dllm_transfer_topk",
+              "dllm_transfer_factor", "dllm_transfer_entropy_bound", "dllm_transfer_edit",
+              "dllm_transfer_schedule", "dllm_block_ranges", "dllm_block_causal_mask"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in _declared_functions():
+        assert hasattr(lib, n), f"{n} is declared but not exported"
+
+
+def test_block_ranges_host_parity(lib):
+    import commit_step_amd as dc
+    for P, G, bl, align in product([0, 1, 31, 32, 77, 100, 1000], [0, 1, 31, 32, 33, 435, 4096],
+                                   [1, 7, 32, 1000], [False, True]):
+        assert dc.block_ranges(P, G, bl, align) == oracle.block_ranges(P, G, bl, align)
+    # partial buffer: the count is still returned, only cap pairs are written
+    buf = (ctypes.c_int64 * 4)()
+    assert lib.dllm_block_ranges(77, 435, 32, 1, buf, 2) == 14
+    assert list(buf) == [64, 96, 96, 128]
+
+
+def _err(lib):
+    return lib.dllm_last_error().decode()
+
+
+def test_token_stats_argument_errors(lib):
+    P = ctypes.c_void_p
+    fake = P(16)   # never dereferenced: every call below fails validation first
+
+    def call(dtype=1, B=1, L=1, V=8, stride=8, T=0.0, step=0, sup=None, nsup=0, rules=None,
+             nrules=0):
+        return lib.dllm_token_stats(fake, dtype, B, L, V, stride, T, 0, step, sup, nsup, fake,
+                                    fake, fake, rules, nrules, fake, 1 << 20, None)
+
+    assert call(dtype=7) == -2 and "dtype" in _err(lib)
+    assert call(B=-1) == -1
+    assert call(V=0) == -1
+    assert call(stride=4) == -1 and "row_stride" in _err(lib)
+    assert call(T=-1.0) == -1 and "temperature" in _err(lib)
+    assert call(T=math.nan) == -1
+    assert call(T=math.inf) == -1
+    assert call(step=1 << 32) == -1 and "step" in _err(lib)
+    assert call(nsup=65) == -1
+    assert call(nsup=1) == -1 and "suppress_ids" in _err(lib)
+    ids = (ctypes.c_int32 * 3)(1, 9, 2)
+    assert call(sup=ids, nsup=2) == -1 and "outside" in _err(lib)
+    ids = (ctypes.c_int32 * 3)(3, 3, 2)
+    assert call(sup=ids, nsup=2) == -1 and "twice" in _err(lib)
+    ids = (ctypes.c_int32 * 8)(*range(8))
+    assert call(sup=ids, nsup=8) == -1 and "every id" in _err(lib)
+    assert call(nrules=3) == -1
+    import commit_step_amd as dc
+    rules = (dc._CRule * 2)()
+    rules[0].kind = 9
+    assert call(rules=rules, nrules=1) == -1 and "kind" in _err(lib)
+    rules[0].kind = dc.RULE_THRESHOLD
+    rules[0].mask = 16
+    rules[0].out = 32
+    rules[0].param = math.nan
+    assert call(rules=rules, nrules=1) == -1 and "NaN" in _err(lib)
+    rules[0].param = 0.5
+    assert call(L=5000, V=8, rules=rules, nrules=1) == -5
+    # empty shapes: OK with nothing launched
+    assert call(B=0) == 0 and call(L=0) == 0
+
+
+def test_transfer_argument_errors(lib):
+    fake = ctypes.c_void_p(16)
+    assert lib.dllm_transfer_threshold(fake, fake, 1, 4, math.nan, 0, ctypes.c_void_p(32), None) == -1
+    assert lib.dllm_transfer_threshold(None, fake, 1, 4, 0.5, 0, ctypes.c_void_p(32), None) == -1
+    assert lib.dllm_transfer_threshold(fake, fake, 1, 4, 0.5, 0, fake, None) == -1   # out aliases conf
+    assert lib.dllm_transfer_factor(fake, fake, -1, 4, 1.0, ctypes.c_void_p(32), None) == -1
+    assert lib.dllm_transfer_entropy_bound(fake, fake, 1, 4097, 1.0, ctypes.c_void_p(32), None) == -5
+    assert lib.dllm_transfer_topk(fake, fake, None, 1, 4, ctypes.c_void_p(32), None) == -1
+    assert lib.dllm_transfer_edit(fake, fake, fake, fake, 1, 4, math.nan, ctypes.c_void_p(32), None) == -1
+    assert lib.dllm_transfer_schedule(fake, 1, 0, fake, None) == -1
+    assert lib.dllm_block_causal_mask(8, 0, fake, None) == -1
+    assert lib.dllm_block_ranges(0, 8, 0, 0, None, 0) == -1
+    assert lib.dllm_block_ranges(-1, 8, 4, 0, None, 0) == -1
+    for fn, args in [(lib.dllm_transfer_threshold, (fake, fake, 0, 4, 0.5, 0, fake, None)),
+                     (lib.dllm_transfer_edit, (fake, fake, fake, fake, 3, 0, 0.5, fake, None)),
+                     (lib.dllm_transfer_schedule, (fake, 0, 4, fake, None)),
+                     (lib.dllm_block_causal_mask, (0, 4, fake, None))]:
+        assert fn(*args) == 0          # empty: nothing launched
+
+
+def test_binding_refuses_cpu_tensors(lib):
+    import torch
+    import commit_step_amd as dc
+    with pytest.raises(ValueError):
+        dc.token_stats(torch.zeros(1, 2, 8))
+    with pytest.raises(ValueError):
+        dc.threshold_transfer(torch.zeros(1, 2), torch.zeros(1, 2, dtype=torch.bool), 0.5)

@@ -1,0 +1,183 @@
+"""GPU parity of dllm_token_stats against the oracle (through the C-ABI binding).
+
+Shapes span several workgroup iterations, ragged tails, the scalar-load path
+(V not a multiple of 8), split rows (few rows, large V) and the largest
+vocabulary of the workloads.
+"""
+import numpy as np
+import pytest
+import torch
+
+import commit_step_amd as dc
+import oracle
+from gpu_util import (assert_sampled_x0, assert_stats, log, stats_np, to_dev)
+from workloads import bf16_bits, random_logits
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("dtype,B,L,V,sup", [
+    ("f32", 2, 3, 1, ()),
+    ("f32", 1, 5, 7, (3,)),
+    ("bf16", 2, 4, 100, (99,)),
+    ("f32", 1, 64, 4096, (4095,)),
+    ("bf16", 3, 5, 5003, (0, 5002)),              # V % 8 != 0: scalar loads
+    ("bf16", 1, 3, 65536 + 24, (65559,)),          # ragged last iteration
+    ("f32", 2, 2, 131072 + 4, ()),                 # split rows, fp32
+    ("bf16", 1, 2, 262144, ()),                    # split rows, largest V
+    ("bf16", 4, 70, 32768, (7, 32767)),            # many rows, 256-thread groups
+    ("f32", 1, 300, 20000, ()),                    # 1024-thread groups
+])
+def test_greedy_parity(dtype, B, L, V, sup):
+    bits, _ = random_logits(100 + V % 97, B, L, V, dtype, 2.5, 0.4, 4.0, 16.0, sup)
+    logits = to_dev(bits, dtype)
+    log(f"greedy {dtype} B={B} L={L} V={V} suppress={sup}")
+    gpu = stats_np(dc.token_stats(logits, suppress_ids=sup))
+    ref = oracle.token_stats(bits, dtype, suppress_ids=sup)
+    assert_stats(gpu, ref, dtype, f"{dtype} {B}x{L}x{V}")
+
+
+def test_row_stride_larger_than_v():
+    B, L, V, pad = 2, 6, 3000, 24
+    bits, _ = random_logits(5, B, L, V + pad, "bf16", 2.0, 0.5, 5.0, 10.0)
+    full = to_dev(bits, "bf16")
+    view = full[:, :, :V]
+    log("row_stride > V")
+    gpu = stats_np(dc.token_stats(view))
+    ref = oracle.token_stats(np.ascontiguousarray(bits[:, :, :V]), "bf16")
+    assert_stats(gpu, ref, "bf16", "strided")
+
+
+def test_peaked_rows_keep_relative_entropy_precision():
+    """Rows whose top logit stands 20..90 nats above the rest: z- is tiny and the
+    entropy must still be accurate relative to its own size."""
+    rng = np.random.default_rng(1)
+    B, L, V = 1, 24, 50000
+    x = rng.standard_normal((B, L, V)).astype(np.float32)
+    for l in range(L):
+        x[0, l, rng.integers(V)] += 20.0 + 3.0 * l
+    log("peaked rows f32")
+    gpu = stats_np(dc.token_stats(to_dev(x)))
+    ref = oracle.token_stats(x, "f32")
+    assert_stats(gpu, ref, "f32", "peaked f32")
+    assert np.all(ref.entropy > 0)
+
+
+def test_exact_ties_at_the_maximum():
+    """Several copies of the row maximum: x0 is the first, prob counts all."""
+    rng = np.random.default_rng(2)
+    B, L, V = 2, 8, 40000
+    x = np.round(rng.standard_normal((B, L, V)) * 2).astype(np.float32)   # many ties
+    for l in range(L):
+        pos = rng.choice(V, size=1 + l, replace=False)
+        x[0, l, pos] = 9.0
+        x[1, l, pos] = 60.0                         # peaked ties
+    bits = bf16_bits(x)
+    for dtype, arr in (("f32", x), ("bf16", bits)):
+        log(f"ties {dtype}")
+        gpu = stats_np(dc.token_stats(to_dev(arr, dtype)))
+        ref = oracle.token_stats(arr, dtype)
+        assert_stats(gpu, ref, dtype, f"ties {dtype}")
+
+
+def _special_rows(V):
+    rows = []
+    r = np.random.default_rng(3).standard_normal(V).astype(np.float32)
+    a = r.copy(); a[[5, 77, V - 1]] = np.nan; rows.append(a)                  # NaN entries
+    rows.append(np.full(V, -np.inf, np.float32))                             # all -inf
+    a = np.full(V, -np.inf, np.float32); a[V // 2] = np.nan; rows.append(a)  # -inf and NaN
+    a = r.copy(); a[[3, 900]] = np.inf; rows.append(a)                       # +inf entries
+    a = r.copy(); a[[3]] = np.inf; a[4] = np.nan; rows.append(a)
+    a = np.full(V, np.nan, np.float32); rows.append(a)                        # all NaN
+    a = r.copy(); a[: V // 2] = -np.inf; rows.append(a)                       # -inf prefix
+    a = r.copy(); a[0] = 1e30; rows.append(a)                                 # huge finite
+    a = np.full(V, -1e30, np.float32); a[V - 1] = -1e30 + 1e24; rows.append(a)
+    return np.stack(rows)[None]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T", [0.0, 0.8])
+def test_nan_and_inf_rows(dtype, T):
+    V = 3000
+    x = _special_rows(V)
+    arr = bf16_bits(x) if dtype == "bf16" else x
+    for sup in ((), (1, 3, 2999)):
+        log(f"special rows {dtype} T={T} suppress={sup}")
+        gpu = stats_np(dc.token_stats(to_dev(arr, dtype), temperature=T, seed=7, step=1,
+                                      suppress_ids=sup))
+        ref = oracle.token_stats(arr, dtype, temperature=T, seed=7, step=1, suppress_ids=sup)
+        assert_stats(gpu, ref, dtype, f"special {dtype} T={T}", x0_exact=(T == 0.0),
+                     mask=(gpu[0] == ref.x0))
+        assert_stats(gpu, ref, dtype, "special entropy", x0_exact=False, fields=("entropy",))
+        if T > 0:
+            pos = [(0, l) for l in range(x.shape[1])]
+            assert_sampled_x0(gpu[0], ref.x0, arr, dtype, T, 7, 1, sup, pos, "special sampled")
+
+
+def test_suppressed_argmax_and_many_ids():
+    rng = np.random.default_rng(4)
+    B, L, V = 2, 6, 70000
+    x = (rng.standard_normal((B, L, V)) * 2).astype(np.float32)
+    sup = tuple(sorted(set(int(v) for v in rng.choice(V, size=62, replace=False)) | {0, V - 1}))
+    for b in range(B):
+        for l in range(L):
+            x[b, l, sup[(b * L + l) % len(sup)]] += 30.0          # suppressed raw argmax
+    bits = bf16_bits(x)
+    log(f"suppress {len(sup)} ids")
+    gpu = stats_np(dc.token_stats(to_dev(bits, "bf16"), suppress_ids=sup))
+    ref = oracle.token_stats(bits, "bf16", suppress_ids=sup)
+    assert_stats(gpu, ref, "bf16", "suppress")
+    assert not np.isin(gpu[0], sup).any()
+
+
+@pytest.mark.parametrize("dtype,B,L,V,T,seed,step", [
+    ("bf16", 2, 16, 8192, 0.7, 1003, 0),
+    ("bf16", 1, 8, 151936, 0.7, 1003, 3),
+    ("f32", 3, 10, 5000, 1.0, 2 ** 40 + 5, 17),
+    ("bf16", 1, 4, 1001, 2.5, 9, 2),               # scalar path
+])
+def test_sampling_parity(dtype, B, L, V, T, seed, step):
+    bits, _ = random_logits(V % 1000 + 1, B, L, V, dtype, 2.5, 0.35, 6.0, 14.0, (V - 1,))
+    logits = to_dev(bits, dtype)
+    log(f"sampling {dtype} B={B} L={L} V={V} T={T} seed={seed} step={step}")
+    gpu = stats_np(dc.token_stats(logits, temperature=T, seed=seed, step=step,
+                                  suppress_ids=(V - 1,)))
+    ref = oracle.token_stats(bits, dtype, temperature=T, seed=seed, step=step,
+                             suppress_ids=(V - 1,))
+    pos = [(b, l) for b in range(B) for l in range(L)]
+    assert_sampled_x0(gpu[0], ref.x0, bits, dtype, T, seed, step, (V - 1,), pos, "sampled")
+    same = gpu[0] == ref.x0
+    assert_stats(gpu, ref, dtype, "sampled stats", mask=same)
+    assert_stats(gpu, ref, dtype, "sampled entropy", x0_exact=False, fields=("entropy",))
+
+
+def test_sampling_is_fresh_per_step_and_zero_temperature_is_greedy():
+    bits, _ = random_logits(8, 1, 64, 4096, "bf16", 1.0)
+    logits = to_dev(bits, "bf16")
+    greedy = stats_np(dc.token_stats(logits))[0]
+    assert np.array_equal(stats_np(dc.token_stats(logits, temperature=0.0, seed=5))[0], greedy)
+    a = stats_np(dc.token_stats(logits, temperature=1.0, seed=5, step=0))[0]
+    b = stats_np(dc.token_stats(logits, temperature=1.0, seed=5, step=1))[0]
+    assert (a != b).mean() > 0.5 and (a != greedy).mean() > 0.5
+
+
+def test_repeated_launches_are_bit_identical():
+    """Race check: fixed reduction orders make every launch identical."""
+    for (B, L, V) in [(1, 3, 262144), (2, 40, 30000)]:
+        bits, rng = random_logits(11, B, L, V, "bf16", 2.0, 0.5, 5.0, 12.0)
+        logits = to_dev(bits, "bf16")
+        cand = torch.from_numpy(rng.random((B, L)) < 0.5).cuda()
+        first = None
+        for i in range(30):
+            r = dc.Rule.entropy_bound(cand, 0.5)
+            st = dc.token_stats(logits, temperature=0.9 if i % 2 else 0.0, seed=3, rules=[r])
+            out = [t.cpu().numpy().copy() for t in (st.x0, st.prob, st.entropy, r.out)]
+            key = i % 2
+            if first is None:
+                first = {}
+            if key not in first:
+                first[key] = out
+            else:
+                for u, v in zip(out, first[key]):
+                    assert np.array_equal(u.view(np.uint8), v.view(np.uint8))
+    log("determinism ok")
