@@ -25,7 +25,9 @@ Readings of the pages taken here (each also listed in the design doc):
 
 Everything is float64, row by row, from the exact input values (bf16 and fp32
 widen to float64 without rounding).  Entropy is the textbook
-H = -sum_v p_v log p_v (terms with p_v = 0 dropped), not a moment formula.
+H = -sum_v p_v log p_v (terms with p_v = 0 dropped), not a moment formula; its
+log z is evaluated as log1p of the non-maximal mass so that it stays accurate
+in float64 when that mass is tiny.
 """
 from collections import namedtuple
 
@@ -82,10 +84,16 @@ def token_stats_row(ell, temperature, seed, step, b, l, suppressed):
     if np.isfinite(m):
         with np.errstate(invalid="ignore", over="ignore"):
             w = np.where(allowed, np.exp(lp - m), 0.0)   # exp(-inf) = 0
-        z = w.sum()
+        # z = 1 + z_minus, z_minus = the mass of every entry but one maximal one;
+        # log z = log1p(z_minus) keeps its accuracy when z_minus is below the
+        # float64 resolution of 1 (a top logit some 40+ nats above the rest).
+        top = _first_argmax(lp, allowed)
+        z_minus = np.sum(np.delete(w, top))
+        z = 1.0 + z_minus
+        log_z = np.log1p(z_minus)
         p = w / z
         keep = allowed & (p > 0.0)
-        H = -np.sum(p[keep] * ((lp[keep] - m) - np.log(z)))
+        H = -np.sum(p[keep] * ((lp[keep] - m) - log_z))
         if sampling:
             with np.errstate(invalid="ignore"):
                 s = lp / temperature + g

@@ -17,8 +17,9 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 MUTATIONS = [
     # (file, original text, mutated text, -k selection of pin tests)
-    ("stats.py", "((lp[keep] - m) - np.log(z))", "(lp[keep] - m)",
+    ("stats.py", "((lp[keep] - m) - log_z)", "(lp[keep] - m)",
      "moment or two_level or uniform"),
+    ("stats.py", "log_z = np.log1p(z_minus)", "log_z = np.log(z)", "peaked"),
     ("stats.py", "H = -np.sum(", "H = np.sum(", "two_level or moment"),
     ("stats.py", "vals == best)[0]", "vals == best)[-1]", "two_level or uniform"),
     ("stats.py", "s = lp / temperature + g", "s = lp * temperature + g",

@@ -61,8 +61,22 @@ def test_two_level_row_closed_form(V, k, a, bv):
     Hc = -k * pa * math.log(pa) - (V - k) * pb * math.log(pb)
     x0, p, H = _stats1(row)
     assert x0 == hi[0]
-    assert p == pytest.approx(pa, rel=1e-13)
-    assert H == pytest.approx(Hc, rel=1e-12)
+    assert p == pytest.approx(pa, rel=1e-13, abs=0)
+    assert H == pytest.approx(Hc, rel=1e-12, abs=0)
+
+
+@pytest.mark.parametrize("V,D", [(1000, 45.0), (50000, 60.0), (7, 300.0)])
+def test_peaked_two_level_row_closed_form(V, D):
+    """One entry D nats above V-1 equal ones: z- = (V-1) e^-D,
+    H = log1p(z-) + D z- / (1 + z-), p = 1 / (1 + z-); exact relative accuracy
+    is required even when z- is far below the float64 resolution of 1."""
+    row = np.zeros(V)
+    row[V // 3] = D
+    zm = (V - 1) * math.exp(-D)
+    x0, p, H = _stats1(row)
+    assert x0 == V // 3
+    assert p == pytest.approx(1.0 / (1.0 + zm), rel=1e-15, abs=0)
+    assert H == pytest.approx(math.log1p(zm) + D * zm / (1.0 + zm), rel=1e-12, abs=0)
 
 
 def test_moment_identities_on_random_rows():
@@ -79,7 +93,7 @@ def test_moment_identities_on_random_rows():
             s2 = math.fsum(e * (row - m))
             assert x0 == int(np.argmax(row))
             assert p == pytest.approx(1.0 / z, rel=1e-12)
-            assert H == pytest.approx(math.log(z) - s2 / z, rel=1e-9, abs=1e-14)
+            assert H == pytest.approx(math.log(z) - s2 / z, rel=1e-9, abs=0)
 
 
 def test_suppress_equals_deleting_the_ids():
