@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Throughput of the fused commit step on one MI355X.
+
+Workload (the configuration the target is quoted on): a DiffusionGemma-like
+canvas, B=1, L=256, V=262144 bf16 logits (workloads.config4), one fused launch
+of dllm_token_stats (greedy) + entropy_bound (gamma 0.5, 154 candidates) +
+edit (tau 0.9, 102 committed positions).  A step is that launch.
+
+Inputs are resident in HBM before the timed region; the launch rotates over
+--rotate copies of the logits (default 8 x 128 MiB = 1 GiB) so the 256 MB
+Infinity Cache cannot serve repeated reads.  Exactly --steps launches are
+timed with HIP events on the stream they are enqueued on.
+
+Prints one JSON line: logit GB/s (value), positions/s, steps/s, the roofline
+of the kernel against the 8 TB/s HBM peak, and the oracle's throughput on
+the host cores (cpu_baseline).
+"""
+import argparse
+import ctypes
+import hashlib
+import glob
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "token_stats_diffusiongemma_canvas_counters.txt")
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=500)
+    p.add_argument("--warmup", type=int, default=50)
+    p.add_argument("--rotate", type=int, default=8, help="distinct copies of the logits")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="minimum host time spent timing the oracle")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="only run a plain 1 GiB device copy (counter calibration)")
+    return p.parse_args()
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    files = sorted(glob.glob(os.path.join(ROOT, "commit_step_amd", "csrc", "*")))
+    files.append(os.path.join(ROOT, "include", "dllm_commit.h"))
+    for f in files:
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode())
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def read_traffic(src_hash):
+    """HBM bytes per launch measured by rocprofv3 counters, if they were taken on
+    the current kernel sources; else None."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as fh:
+            for ln in fh:
+                if "=" in ln and not ln.startswith("#"):
+                    k, v = ln.strip().split("=", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("kernel_source_sha256") != src_hash:
+            return None
+        return float(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def copy_probe():
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
+
+
+def cpu_baseline(w, logit_bytes, min_seconds):
+    """The oracle as it stands, on the same canvas, single process."""
+    import numpy as np
+    import oracle
+    p = w.params
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        st = oracle.token_stats(w.logits, "bf16")
+        oracle.entropy_bound_transfer(st.entropy.astype(np.float32), w.cand, p["gamma"])
+        oracle.edit_transfer(st.x0, st.prob.astype(np.float32), w.tokens, w.editable, p["tau_edit"])
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    B, L, V = w.shape
+    return {"value": round(logit_bytes * reps / el / 1e9, 4), "unit": "GB/s",
+            "positions_per_s": round(B * L * reps / el, 2), "cores": 1, "kind": "oracle",
+            "seconds": round(el, 2),
+            "sample": f"the full canvas ({B}x{L}x{V} bf16) with entropy_bound and edit, "
+                      f"{reps} repetition(s), numpy float64 oracle in one process"}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: --gpus {args.gpus}: this benchmark runs on exactly one GPU; the commit "
+              "step shards batch rows across GPUs with no communication, so a multi-GPU figure "
+              "is the one-GPU figure times N and is not measured here.", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_probe:
+        copy_probe()
+        return
+
+    import numpy as np
+    import torch
+
+    import commit_step_amd as dc
+    import workloads
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    w = workloads.config4()
+    B, L, V = w.shape
+    p = w.params
+    R = max(1, args.rotate)
+    base = torch.from_numpy(w.logits.view(np.int16)).view(torch.bfloat16).to(dev)
+    rot = torch.empty((R, B, L, V), dtype=torch.bfloat16, device=dev)
+    for i in range(R):
+        rot[i].copy_(base)
+    del base
+    cand = torch.from_numpy(w.cand).to(dev)
+    editable = torch.from_numpy(w.editable).to(dev)
+    tokens = torch.from_numpy(w.tokens).to(dev)
+    x0 = torch.empty((B, L), dtype=torch.int32, device=dev)
+    prob = torch.empty((B, L), dtype=torch.float32, device=dev)
+    ent = torch.empty((B, L), dtype=torch.float32, device=dev)
+    eb_out = torch.empty((B, L), dtype=torch.bool, device=dev)
+    ed_out = torch.empty((B, L), dtype=torch.bool, device=dev)
+
+    lib = dc.load_library()
+    ws_bytes = int(lib.dllm_token_stats_workspace_size(dc.DLLM_BF16, B, L, V))
+    ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    rules = (dc._CRule * 2)()
+    rules[0].kind, rules[0].mask, rules[0].out = dc.RULE_ENTROPY_BOUND, cand.data_ptr(), eb_out.data_ptr()
+    rules[0].param = p["gamma"]
+    rules[1].kind, rules[1].mask, rules[1].out = dc.RULE_EDIT, editable.data_ptr(), ed_out.data_ptr()
+    rules[1].param, rules[1].tokens = p["tau_edit"], tokens.data_ptr()
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    call_args = [(rot[i].data_ptr(), dc.DLLM_BF16, B, L, V, V, 0.0, 0, 0, None, 0,
+                  x0.data_ptr(), prob.data_ptr(), ent.data_ptr(), rules, 2, ws.data_ptr(),
+                  ws.numel(), stream) for i in range(R)]
+    fn = lib.dllm_token_stats
+
+    rc = 0
+    for i in range(args.warmup):
+        rc |= fn(*call_args[i % R])
+    torch.cuda.synchronize()
+    if rc:
+        raise RuntimeError(lib.dllm_last_error().decode())
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        rc |= fn(*call_args[i % R])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if rc:
+        raise RuntimeError(lib.dllm_last_error().decode())
+    ms = start.elapsed_time(end) / args.steps
+
+    logit_bytes = B * L * V * 2
+    per_position = 1 + 1 + 4 + 12 + 1 + 1        # cand, editable, tokens in; stats, masks out
+    alg_bytes = logit_bytes + B * L * per_position
+    achieved = alg_bytes / (ms * 1e-3) / 1e9
+    src_hash = kernel_source_hash()
+    line = {
+        "metric": "logit GB/s and positions/sec for token_stats+transfer; % of HBM peak",
+        "value": round(logit_bytes / (ms * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "diffusiongemma_canvas: fused token_stats (greedy) + "
+                               "entropy_bound(gamma=0.5) + edit(tau=0.9)",
+                   "B": B, "L": L, "V": V, "logits": "bf16", "rotated_copies": R},
+        "positions_per_s": round(B * L / (ms * 1e-3), 1),
+        "steps_per_s": round(1e3 / ms, 1),
+        "pct_hbm_peak": round(100.0 * achieved / HBM_PEAK_GBS, 2),
+        "host_wall_ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": read_traffic(src_hash),
+                     "kernel": "token_stats_kernel<bf16, 1024 threads, greedy, 16-byte loads>",
+                     "algorithmic_bytes_per_launch": alg_bytes},
+        "kernel_source_sha256": src_hash,
+    }
+    line["cpu_baseline"] = None if args.no_cpu_baseline else \
+        cpu_baseline(w, logit_bytes, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

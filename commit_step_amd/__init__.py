@@ -166,6 +166,28 @@ def _k_tensor(k, B, device):
     return torch.full((B,), int(k), dtype=torch.int32, device=device)
 
 
+def _row_stride(logits):
+    """Elements between consecutive positions of (B, L, V) logits.  Sizes 0 and
+    1 carry no stride information; otherwise the rows must be unit-stride and
+    evenly spaced (position (b, l) at (b * L + l) * row_stride)."""
+    B, L, V = logits.shape
+    if B * L * V == 0:
+        return max(V, 1)
+    if V > 1 and logits.stride(2) != 1:
+        raise ValueError("logits rows must be contiguous (unit stride along V)")
+    if L > 1:
+        rs = logits.stride(1)
+    elif B > 1:
+        rs = logits.stride(0)
+    else:
+        rs = V
+    if B > 1 and logits.stride(0) != L * rs:
+        raise ValueError("logits positions must be evenly strided: stride(0) == L * stride(1)")
+    if rs < V:
+        raise ValueError("logits rows overlap (row stride < V)")
+    return rs
+
+
 def token_stats(logits, temperature=0.0, seed=None, step=0, suppress_ids=(), rules=(),
                 out=None, workspace=None):
     """Per-position (x0, prob, entropy) of (B, L, V) float32 / bfloat16 logits.
@@ -181,8 +203,7 @@ def token_stats(logits, temperature=0.0, seed=None, step=0, suppress_ids=(), rul
     if logits.dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("logits must be float32 or bfloat16")
     B, L, V = logits.shape
-    if logits.stride(2) != 1 or logits.stride(0) != L * logits.stride(1):
-        raise ValueError("logits rows must be contiguous and evenly strided")
+    row_stride = _row_stride(logits)
     if temperature > 0 and seed is None:
         raise ValueError("sampling (temperature > 0) needs an explicit seed")
     dev = logits.device
@@ -219,7 +240,7 @@ def token_stats(logits, temperature=0.0, seed=None, step=0, suppress_ids=(), rul
         need = int(lib.dllm_token_stats_workspace_size(dt, B, L, V))
         ws = workspace if workspace is not None else _workspace(dev, need)
         _check(lib.dllm_token_stats(
-            logits.data_ptr(), dt, B, L, V, logits.stride(1), float(temperature),
+            logits.data_ptr(), dt, B, L, V, row_stride, float(temperature),
             int(seed or 0) & 0xFFFFFFFFFFFFFFFF, int(step), sup, len(suppress_ids),
             x0.data_ptr(), prob.data_ptr(), ent.data_ptr(),
             crules if len(rules) else None, len(rules), ws.data_ptr(), ws.numel(),

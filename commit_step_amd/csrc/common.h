@@ -199,10 +199,14 @@ __device__ __host__ __forceinline__ Fx fx_from_f32_bits(uint32_t u) {
   const uint32_t e = (u >> 23) & 0xffu, frac = u & 0x7fffffu;
   const uint64_t m = e ? (uint64_t)(frac | 0x800000u) : (uint64_t)frac;
   if (m == 0) return r;
-  const int sh = (e ? (int)e : 1) - 1;              // 0 .. 253
-  const int limb = sh >> 6, off = sh & 63;
-  r.w[limb] = m << off;
-  if (off > 40 && limb < 4) r.w[limb + 1] = m >> (64 - off);
+  const int sh = (e ? (int)e : 1) - 1;              // 0 .. 253: value = m * 2^sh units
+  // limb i holds bits [64 i, 64 i + 64): m shifted by sh - 64 i (constant i, so
+  // every limb stays in a register)
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const int s = sh - 64 * i;
+    r.w[i] = (s >= 0 && s < 64) ? (m << s) : (s < 0 && s > -24) ? (m >> -s) : 0ull;
+  }
   if (u & 0x80000000u) fx_negate(r);
   return r;
 }

@@ -1,13 +1,24 @@
-// Commit rules over one batch row, run by one workgroup (any multiple of 64
-// threads).  Shared by the standalone dllm_transfer_* kernels and by the fused
-// path of dllm_token_stats, where the last workgroup to finish a batch row runs
-// them on the statistics the whole launch has just written.
+// Commit rules over one batch row, run by one workgroup.  Shared by the
+// standalone dllm_transfer_* kernels and by the fused path of
+// dllm_token_stats, where the last workgroup to finish a batch row runs them on
+// the statistics the launch has just written.
 //
 // Rankings: every candidate gets a 64-bit key (order-preserving float bits in
-// the high word, position in the low word) and a workgroup bitonic sort in LDS
-// orders them; equal scores therefore keep the lower position first (stable
-// order, "Deviations from the references").  Non-candidates get the all-ones
-// key and sort last.
+// the high word, position in the low word), so ascending key order is the
+// stable order of "Deviations from the references" (equal scores: lower
+// position first), and the rank of a candidate (the number of candidate keys
+// below its own) is its index in the sorted order.
+//   * Short rows (L <= blockDim.x, one position per thread): the candidates are
+//     compacted into an LDS list and each rank is an all-pairs count over it
+//     with broadcast reads: one dependent phase, no sorting network.  For
+//     entropy_bound only candidates with H <= gamma can be followed by another
+//     committed candidate (entropies are >= 0), so ranks and prefix sums run
+//     over that subset plus the smallest entropy above gamma.
+//   * Long rows, and entropy rows with negative or non-finite entropies, use a
+//     workgroup bitonic sort in LDS.
+// The score arrays are read with agent-scope atomic loads (coherent across
+// XCDs), because in the fused path they were written moments before by other
+// workgroups of the same launch.
 #pragma once
 
 #include "common.h"
@@ -15,7 +26,6 @@
 namespace dllm {
 
 constexpr uint64_t kSentinel = ~0ull;
-constexpr int kScanThreads = 256;
 
 // Host-prepared view of one rule.
 struct RuleDev {
@@ -26,8 +36,8 @@ struct RuleDev {
   const int32_t *k;
   const int32_t *tokens;
   double param;
-  // ENTROPY_BOUND: floor(gamma * 2^149) as a signed fixed-point number, and
-  // how to compare a finite sum with gamma: 0 = use gamma_fx, 1 = always <=
+  // ENTROPY_BOUND, exact comparison of a finite sum with gamma: floor(gamma *
+  // 2^149) as a signed fixed-point number, and 0 = use gamma_fx, 1 = always <=
   // (gamma >= 2^141 or +inf), 2 = never <= (gamma <= -2^141 or -inf).
   Fx gamma_fx;
   int gamma_class;
@@ -40,48 +50,38 @@ __host__ __device__ inline int rule_pow2(int L) {
   return n;
 }
 
-// LDS bytes the rule routines need for a batch row of L positions.
-__host__ __device__ inline size_t rule_smem_bytes(int L) {
-  const size_t keys = (size_t)rule_pow2(L) * 8;
-  const size_t bytes = ((size_t)L + 15) & ~(size_t)15;
-  return keys + bytes + kScanThreads * sizeof(Fx) + 64;
+// LDS bytes the rule routines need for a batch row of L positions run by nt
+// threads.
+__host__ __device__ inline size_t rule_smem_bytes(int L, int nt) {
+  const size_t Np = (size_t)rule_pow2(L);
+  const size_t lists = Np * 16 + (size_t)nt * 12;   // short rows
+  const size_t keys = Np * 8;                        // sorting network
+  return (((lists > keys ? lists : keys) + 7) & ~(size_t)7) + 512;
 }
 
 struct RuleSmem {
-  uint64_t *keys;     // [Np]
-  uint8_t *commit;    // [L]
-  Fx *scan;           // [kScanThreads]
-  int *misc;          // [16]
+  uint64_t *keys;     // [Np] sorted keys (long rows) / compacted list (short rows)
+  double *hs;         // [Np] values matching the list (short rows)
+  double *part_sum;   // [nt] (also the query keys of block_rank)
+  int *part_cnt;      // [nt]
+  int *misc;          // [64]
 };
 
 __device__ inline RuleSmem rule_smem(unsigned char *base, int L) {
   RuleSmem s;
-  const int Np = rule_pow2(L);
+  const size_t Np = (size_t)rule_pow2(L), nt = blockDim.x;
   s.keys = reinterpret_cast<uint64_t *>(base);
-  s.commit = base + (size_t)Np * 8;
-  s.scan = reinterpret_cast<Fx *>(base + (size_t)Np * 8 + (((size_t)L + 15) & ~(size_t)15));
-  s.misc = reinterpret_cast<int *>(s.scan + kScanThreads);
+  s.hs = reinterpret_cast<double *>(base + Np * 8);
+  s.part_sum = reinterpret_cast<double *>(base + Np * 16);
+  s.part_cnt = reinterpret_cast<int *>(base + Np * 16 + nt * 8);
+  const size_t lists = Np * 16 + nt * 12;
+  const size_t top = lists > Np * 8 ? lists : Np * 8;
+  s.misc = reinterpret_cast<int *>(base + ((top + 7) & ~(size_t)7));
   return s;
 }
 
-// Bitonic sort of Np keys, ascending.
-__device__ inline void block_bitonic_sort(uint64_t *keys, int Np) {
-  const int tid = threadIdx.x, nt = blockDim.x;
-  for (int k = 2; k <= Np; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < (Np >> 1); i += nt) {
-        const int lo = ((i & ~(j - 1)) << 1) | (i & (j - 1));
-        const int hi = lo | j;
-        const bool asc = (lo & k) == 0;
-        const uint64_t a = keys[lo], b = keys[hi];
-        if ((a > b) == asc) {
-          keys[lo] = b;
-          keys[hi] = a;
-        }
-      }
-      __syncthreads();
-    }
-  }
+__device__ __forceinline__ float load_coherent(const float *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // (i + 1) * (1 - c) <= f, exactly: (i+1)*c is exact in float64 (a 24-bit
@@ -104,171 +104,338 @@ __device__ inline bool factor_holds(int i, float c, double f) {
   return s < f || (s == f && e <= 0.0);
 }
 
-// Write the batch row's commit bytes from LDS to global memory.
-__device__ inline void write_commit(const RuleSmem &sm, uint8_t *out_row, int L) {
-  for (int l = threadIdx.x; l < L; l += blockDim.x) out_row[l] = sm.commit[l];
+// Does S_i <= gamma hold, given [finite part of S_i <= gamma] and the number
+// of -inf / +inf entropies among the first i sorted candidates?
+__device__ __forceinline__ bool ent_prefix_ok(const RuleDev &r, bool finite_le, int n_neg,
+                                              int n_pos) {
+  if (n_neg && n_pos) return false;
+  if (n_pos) return r.gamma_is_pos_inf != 0;
+  if (n_neg) return true;
+  if (r.gamma_class == 1) return true;
+  if (r.gamma_class == 2) return false;
+  return finite_le;
+}
+
+// Exact first index i at which the prefix sum sum_{j<i} h[j] of finite,
+// non-negative float32 values (in sorted order, in LDS) exceeds gamma; n if
+// none.  One thread walks the list in fixed point: the rare path taken when a
+// float64 prefix lands within its rounding bound of gamma.
+__device__ inline int exact_first_fail(const RuleDev &r, const float *h, int n, int *slot) {
+  if (threadIdx.x == 0) {
+    Fx s;
+    fx_zero(s);
+    int upto = n;
+    for (int i = 0; i < n; ++i) {
+      if (!fx_le(s, r.gamma_fx)) { upto = i; break; }
+      fx_add(s, fx_from_f32_bits(__float_as_uint(h[i])));
+    }
+    *slot = upto;
+  }
+  __syncthreads();
+  const int v = *slot;
+  __syncthreads();
+  return v;
+}
+
+// ---------------------------------------------------------------- short rows
+
+__device__ __forceinline__ int lane_prefix(uint64_t m) {   // set bits below this lane
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+}
+
+// Appends the `pred` threads' values to list[] in thread order and returns the
+// count.  Every thread must call it (wcnt: 16 ints of LDS).
+template <typename V>
+__device__ inline int block_compact(bool pred, V val, V *list, int *wcnt) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const uint64_t m = __builtin_amdgcn_ballot_w64(pred);
+  if (lane == 0) wcnt[wave] = __builtin_popcountll(m);
+  __syncthreads();
+  int off = 0, total = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int c = wcnt[w];
+    off += w < wave ? c : 0;
+    total += c;
+  }
+  if (pred) list[off + lane_prefix(m)] = val;
+  __syncthreads();
+  return total;
+}
+
+// For the query keys q (thread i < nq holds query i), the number of list keys
+// below the query and the float64 sum of their values (when vals is given).
+// G = blockDim.x / P threads share a query, each counting one part of the
+// list; the owner (thread i < P) returns the totals.  Requires nq <= P.
+__device__ inline int block_rank(uint64_t q, int nq, const uint64_t *list, int n,
+                                 const double *vals, double *sum, const RuleSmem &sm, int P) {
+  const int t = threadIdx.x, G = blockDim.x / P, part = t / P, i = t - part * P;
+  const int per = (n + G - 1) / G;
+  const int j0 = min(part * per, n), j1 = min(j0 + per, n);
+  uint64_t *qk = reinterpret_cast<uint64_t *>(sm.part_sum);
+  if (G > 1) {
+    if (part == 0 && i < nq) qk[i] = q;
+    __syncthreads();
+  }
+  const uint64_t myq = G > 1 ? (i < nq ? qk[i] : kSentinel) : q;
+  if (G > 1) __syncthreads();
+  int cnt = 0;
+  double s = 0.0;
+  if (i < nq) {
+    if (vals) {
+      for (int j = j0; j < j1; ++j) {
+        const bool lt = list[j] < myq;
+        cnt += lt;
+        s += lt ? vals[j] : 0.0;
+      }
+    } else {
+#pragma unroll 4
+      for (int j = j0; j < j1; ++j) cnt += list[j] < myq;
+    }
+  }
+  if (G > 1) {
+    if (part > 0 && i < nq) { sm.part_cnt[t] = cnt; sm.part_sum[t] = s; }
+    __syncthreads();
+    if (part == 0 && i < nq)
+      for (int g = 1; g < G; ++g) { cnt += sm.part_cnt[g * P + i]; s += sm.part_sum[g * P + i]; }
+    __syncthreads();
+  }
+  if (sum) *sum = s;
+  return cnt;
+}
+
+__device__ __forceinline__ int owners_for(int n, int nt) {
+  int P = 64;
+  while (P < n) P <<= 1;
+  return P < nt ? P : nt;
+}
+
+// topk / factor on a short row.
+__device__ inline void short_rank_rule(const RuleDev &r, int b, int L, const float *conf,
+                                       const RuleSmem &sm) {
+  const int t = threadIdx.x;
+  const uint8_t *m_row = r.mask + (int64_t)b * L;
+  uint8_t *o_row = r.out + (int64_t)b * L;
+  const bool cand = t < L && m_row[t];
+  const float c = cand ? conf_sanitized(load_coherent(conf + (int64_t)b * L + t)) : 0.f;
+  const uint64_t key = cand ? (((uint64_t)conf_key(c) << 32) | (uint32_t)t) : kSentinel;
+  int *ff = sm.misc + 20;
+  if (t == 0) *ff = 0x7fffffff;
+  const int n = block_compact(cand, key, sm.keys, sm.misc);
+  const int P = owners_for(n, blockDim.x);
+  const uint64_t q = t < n ? sm.keys[t] : kSentinel;
+  const int rank = block_rank(q, n, sm.keys, n, nullptr, nullptr, sm, P);
+  int n_commit;
+  if (r.kind == DLLM_RULE_TOPK) {
+    const int k = r.k[b];
+    n_commit = k < 0 ? 0 : (k > n ? n : k);
+  } else {
+    if (t < n && !factor_holds(rank, conf_from_key((uint32_t)(q >> 32)), r.param)) atomicMin(ff, rank);
+    __syncthreads();
+    const int first = *ff;
+    n_commit = n ? max(first < n ? first : n, 1) : 0;
+  }
+  if (t < n) o_row[(uint32_t)q] = rank < n_commit ? 1 : 0;
+  if (t < L && !m_row[t]) o_row[t] = 0;
+}
+
+// entropy_bound on a short row whose candidate entropies are all finite and
+// >= 0.  Returns false (nothing written) when the subset H <= gamma is too
+// large for the all-pairs pass; the caller then takes the sorted path.
+__device__ inline bool short_entropy_rule(const RuleDev &r, int b, int L, const float *ent,
+                                          const RuleSmem &sm) {
+  const int t = threadIdx.x, nt = blockDim.x;
+  const uint8_t *m_row = r.mask + (int64_t)b * L;
+  uint8_t *o_row = r.out + (int64_t)b * L;
+  const bool cand = t < L && m_row[t];
+  const float h = cand ? load_coherent(ent + (int64_t)b * L + t) : 0.f;
+  const uint64_t key = cand ? (((uint64_t)ent_key(h) << 32) | (uint32_t)t) : kSentinel;
+  const bool in_f = cand && (double)h <= r.param;
+  unsigned long long *next = reinterpret_cast<unsigned long long *>(sm.misc + 24);
+  int *ff = sm.misc + 20;
+  int *slot = sm.misc + 22;
+  if (t == 0) { *next = kSentinel; *ff = 0x7fffffff; }
+  __syncthreads();
+  // the smallest key among the candidates above gamma
+  if (cand && !in_f) atomicMin(next, (unsigned long long)key);
+  const int nF = block_compact(in_f, key, sm.keys, sm.misc);
+  const uint64_t nxt = *next;
+  const int nc = nF + (int)__syncthreads_count(cand && !in_f);
+  if (nF + 1 > nt || nF > 1024) return false;
+  if (t < nF) sm.hs[t] = (double)ent_from_key((uint32_t)(sm.keys[t] >> 32));
+  __syncthreads();
+  // queries: every key of F, then the smallest key above gamma (index nF)
+  const bool has_next = nxt != kSentinel;
+  const int nq = nF + (has_next ? 1 : 0);
+  const uint64_t q = t < nF ? sm.keys[t] : (t == nF && has_next ? nxt : kSentinel);
+  const int P = owners_for(nq, nt);
+  double S = 0.0;
+  const int rank = block_rank(q, nq, sm.keys, nF, sm.hs, &S, sm, P);
+  // Entropies are >= 0, so sum |h| = S: |S - exact| <= (terms + 64) 2^-53 S
+  // whatever the summation order.
+  const double err = (double)(nF + 64) * 0x1p-52 * S;
+  const bool live = t < nq;
+  const bool uncertain = live && r.gamma_class == 0 && err != 0.0 && fabs(S - r.param) <= err;
+  bool fails = live && !ent_prefix_ok(r, S <= r.param, 0, 0);
+  if (__syncthreads_count(uncertain)) {
+    // rare: decide the prefixes exactly, in rank order
+    float *hsorted = reinterpret_cast<float *>(sm.part_cnt);
+    if (live) hsorted[rank] = ent_from_key((uint32_t)(q >> 32));
+    __syncthreads();
+    const int upto = exact_first_fail(r, hsorted, nq, slot);
+    fails = live && !ent_prefix_ok(r, rank < upto, 0, 0);
+  }
+  if (fails) atomicMin(ff, rank);
+  __syncthreads();
+  const int first = *ff;
+  // No failure up to the smallest entropy above gamma: the candidate after it
+  // fails (its prefix holds an entropy above gamma), or the row ends.
+  const int n_star = first != 0x7fffffff ? first : min(nF + 1, nc);
+  const int n_commit = nc ? max(n_star, 1) : 0;
+  if (live) o_row[(uint32_t)q] = rank < n_commit ? 1 : 0;
+  if (t < L && cand && !in_f && key != nxt) o_row[t] = 0;
+  if (t < L && !cand) o_row[t] = 0;
+  return true;
+}
+
+// ---------------------------------------------------------------- long rows
+
+// Plain LDS bitonic sort of Np keys, ascending.
+__device__ inline void block_sort_lds(uint64_t *keys, int Np) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  for (int k = 2; k <= Np; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < (Np >> 1); i += nt) {
+        const int lo = ((i & ~(j - 1)) << 1) | (i & (j - 1));
+        const int hi = lo | j;
+        const bool asc = (lo & k) == 0;
+        const uint64_t a = keys[lo], b = keys[hi];
+        if ((a > b) == asc) {
+          keys[lo] = b;
+          keys[hi] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// Sorted candidate keys of batch row b in sm.keys[0..nc); returns nc.
+__device__ inline int sort_candidates(const RuleDev &r, int b, int L, const float *score,
+                                      bool by_entropy, const RuleSmem &sm) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int Np = rule_pow2(L);
+  const float *s_row = score + (int64_t)b * L;
+  const uint8_t *m_row = r.mask + (int64_t)b * L;
+  int *cnt = sm.misc + 4;
+  if (tid == 0) *cnt = 0;
+  __syncthreads();
+  int mine = 0;
+  for (int i = tid; i < Np; i += nt) {
+    uint64_t key = kSentinel;
+    if (i < L && m_row[i]) {
+      const float v = load_coherent(s_row + i);
+      const uint32_t hk = by_entropy ? ent_key(v) : conf_key(v);
+      key = ((uint64_t)hk << 32) | (uint32_t)i;
+      ++mine;
+    }
+    sm.keys[i] = key;
+  }
+  if (mine) atomicAdd(cnt, mine);
+  __syncthreads();
+  const int nc = *cnt;
+  block_sort_lds(sm.keys, Np);
+  return nc;
+}
+
+// Commit the first n of the nc sorted candidates; zero every other position.
+__device__ inline void commit_sorted(const RuleDev &r, int b, int L, int n, int nc,
+                                     const RuleSmem &sm) {
+  uint8_t *o_row = r.out + (int64_t)b * L;
+  const uint8_t *m_row = r.mask + (int64_t)b * L;
+  for (int i = threadIdx.x; i < nc; i += blockDim.x) o_row[(uint32_t)sm.keys[i]] = i < n ? 1 : 0;
+  for (int l = threadIdx.x; l < L; l += blockDim.x)
+    if (!m_row[l]) o_row[l] = 0;
+}
+
+__device__ inline void long_rank_rule(const RuleDev &r, int b, int L, const float *conf,
+                                      const RuleSmem &sm) {
+  const int nc = sort_candidates(r, b, L, conf, false, sm);
+  int n;
+  if (r.kind == DLLM_RULE_TOPK) {
+    const int k = r.k[b];
+    n = k < 0 ? 0 : (k > nc ? nc : k);
+  } else {
+    int *first_fail = sm.misc + 6;
+    if (threadIdx.x == 0) *first_fail = nc;
+    __syncthreads();
+    for (int i = threadIdx.x; i < nc; i += blockDim.x)
+      if (!factor_holds(i, conf_from_key((uint32_t)(sm.keys[i] >> 32)), r.param))
+        atomicMin(first_fail, i);
+    __syncthreads();
+    n = nc ? max(*first_fail, 1) : 0;
+  }
+  commit_sorted(r, b, L, n, nc, sm);
+}
+
+// entropy_bound on the sorted candidates, for any entropies (NaN counts as
+// +inf): exact sequential walk in fixed point by one thread.
+__device__ inline void long_entropy_rule(const RuleDev &r, int b, int L, const float *ent,
+                                         const RuleSmem &sm) {
+  const int nc = sort_candidates(r, b, L, ent, true, sm);
+  int *first_fail = sm.misc + 6;
+  if (threadIdx.x == 0) {
+    int n_neg_all = 0, n_pos_all = 0;
+    for (int i = 0; i < nc; ++i) {
+      const uint32_t u = __float_as_uint(ent_from_key((uint32_t)(sm.keys[i] >> 32)));
+      n_neg_all += u == 0xff800000u;
+      n_pos_all += u == 0x7f800000u;
+    }
+    Fx s;
+    fx_zero(s);
+    int ff = nc;
+    for (int i = 0; i < nc; ++i) {
+      const int n_neg = min(i, n_neg_all), n_pos = max(0, i - (nc - n_pos_all));
+      const bool fle = r.gamma_class == 0 ? fx_le(s, r.gamma_fx) : true;
+      if (!ent_prefix_ok(r, fle, n_neg, n_pos)) { ff = i; break; }
+      const uint32_t u = __float_as_uint(ent_from_key((uint32_t)(sm.keys[i] >> 32)));
+      if (bits_finite(u)) fx_add(s, fx_from_f32_bits(u));
+    }
+    *first_fail = ff;
+  }
+  __syncthreads();
+  const int n = nc ? max(*first_fail, 1) : 0;
+  commit_sorted(r, b, L, n, nc, sm);
 }
 
 // threshold: no ranking needed.
 __device__ inline void rule_threshold(const RuleDev &r, int b, int L, const float *conf,
                                       const RuleSmem &sm) {
   const int tid = threadIdx.x, nt = blockDim.x;
-  uint64_t *best = reinterpret_cast<uint64_t *>(sm.misc);    // misc[0..1]
+  unsigned long long *best = reinterpret_cast<unsigned long long *>(sm.misc + 24);
   int *n_pass = sm.misc + 2;
   if (tid == 0) { *best = kSentinel; *n_pass = 0; }
   __syncthreads();
   const float *c_row = conf + (int64_t)b * L;
   const uint8_t *m_row = r.mask + (int64_t)b * L;
+  uint8_t *o_row = r.out + (int64_t)b * L;
   int my_pass = 0;
   uint64_t my_best = kSentinel;
   for (int l = tid; l < L; l += nt) {
     uint8_t v = 0;
     if (m_row[l]) {
-      const float c = conf_sanitized(c_row[l]);
+      const float c = conf_sanitized(load_coherent(c_row + l));
       const double cd = (double)c;
       v = (r.strict ? (cd > r.param) : (cd >= r.param)) ? 1 : 0;
       my_pass += v;
       const uint64_t key = ((uint64_t)conf_key(c) << 32) | (uint32_t)l;
       my_best = key < my_best ? key : my_best;
     }
-    sm.commit[l] = v;
+    o_row[l] = v;
   }
   if (my_pass) atomicAdd(n_pass, my_pass);
-  if (my_best != kSentinel) atomicMin(reinterpret_cast<unsigned long long *>(best),
-                                      (unsigned long long)my_best);
+  if (my_best != kSentinel) atomicMin(best, (unsigned long long)my_best);
   __syncthreads();
-  if (tid == 0 && *n_pass == 0 && *best != kSentinel) sm.commit[(uint32_t)*best] = 1;
-  __syncthreads();
-  write_commit(sm, r.out + (int64_t)b * L, L);
-}
-
-// Load the candidates' ranking keys and sort them; returns the candidate count.
-__device__ inline int load_and_sort(const RuleDev &r, int b, int L, const float *score,
-                                    bool by_entropy, const RuleSmem &sm) {
-  const int tid = threadIdx.x, nt = blockDim.x;
-  const int Np = rule_pow2(L);
-  int *n_cand = sm.misc + 4;
-  if (tid == 0) *n_cand = 0;
-  __syncthreads();
-  const float *s_row = score + (int64_t)b * L;
-  const uint8_t *m_row = r.mask + (int64_t)b * L;
-  int mine = 0;
-  for (int i = tid; i < Np; i += nt) {
-    uint64_t key = kSentinel;
-    if (i < L) {
-      if (m_row[i]) {
-        const uint32_t hk = by_entropy ? ent_key(s_row[i]) : conf_key(s_row[i]);
-        key = ((uint64_t)hk << 32) | (uint32_t)i;
-        ++mine;
-      }
-      sm.commit[i] = 0;
-    }
-    sm.keys[i] = key;
-  }
-  if (mine) atomicAdd(n_cand, mine);
-  __syncthreads();
-  block_bitonic_sort(sm.keys, Np);
-  return *n_cand;
-}
-
-// Commit the first n keys of the sorted order.
-__device__ inline void commit_prefix(const RuleDev &r, int b, int L, int n, const RuleSmem &sm) {
-  for (int i = threadIdx.x; i < n; i += blockDim.x) sm.commit[(uint32_t)sm.keys[i]] = 1;
-  __syncthreads();
-  write_commit(sm, r.out + (int64_t)b * L, L);
-}
-
-__device__ inline void rule_topk(const RuleDev &r, int b, int L, const float *conf,
-                                 const RuleSmem &sm) {
-  const int nc = load_and_sort(r, b, L, conf, false, sm);
-  int k = r.k[b];
-  k = k < 0 ? 0 : (k > nc ? nc : k);
-  commit_prefix(r, b, L, k, sm);
-}
-
-__device__ inline void rule_factor(const RuleDev &r, int b, int L, const float *conf,
-                                   const RuleSmem &sm) {
-  const int nc = load_and_sort(r, b, L, conf, false, sm);
-  int *first_fail = sm.misc + 6;
-  if (threadIdx.x == 0) *first_fail = nc;
-  __syncthreads();
-  for (int i = threadIdx.x; i < nc; i += blockDim.x) {
-    const float c = conf_from_key((uint32_t)(sm.keys[i] >> 32));
-    if (!factor_holds(i, c, r.param)) atomicMin(first_fail, i);
-  }
-  __syncthreads();
-  const int n = nc ? max(*first_fail, 1) : 0;
-  commit_prefix(r, b, L, n, sm);
-}
-
-// Does the exclusive prefix sum S_i (finite part `fin`, plus the -inf / +inf
-// entries among the first i sorted candidates) satisfy S_i <= gamma?
-__device__ inline bool ent_prefix_ok(const RuleDev &r, const Fx &fin, int n_neg, int n_pos) {
-  if (n_neg && n_pos) return false;
-  if (n_pos) return r.gamma_is_pos_inf != 0;
-  if (n_neg) return true;
-  if (r.gamma_class == 1) return true;
-  if (r.gamma_class == 2) return false;
-  return fx_le(fin, r.gamma_fx);
-}
-
-__device__ inline void rule_entropy_bound(const RuleDev &r, int b, int L, const float *ent,
-                                          const RuleSmem &sm) {
-  const int nc = load_and_sort(r, b, L, ent, true, sm);
-  const int tid = threadIdx.x;
-  int *first_fail = sm.misc + 6;
-  int *n_neg_all = sm.misc + 7;
-  int *n_pos_all = sm.misc + 8;
-  if (tid == 0) { *first_fail = nc; *n_neg_all = 0; *n_pos_all = 0; }
-  __syncthreads();
-  // Sorted ascending: the -inf entropies come first and the +inf ones last.
-  for (int i = tid; i < nc; i += blockDim.x) {
-    const uint32_t u = __float_as_uint(ent_from_key((uint32_t)(sm.keys[i] >> 32)));
-    if (u == 0xff800000u) atomicAdd(n_neg_all, 1);
-    if (u == 0x7f800000u) atomicAdd(n_pos_all, 1);
-  }
-  // Each of the first kScanThreads threads owns one contiguous segment.
-  const int seg = (nc + kScanThreads - 1) / kScanThreads;
-  const int lo = tid * seg, hi = min(lo + seg, nc);
-  Fx local;
-  fx_zero(local);
-  if (tid < kScanThreads) {
-    for (int i = lo; i < hi; ++i) {
-      const uint32_t u = __float_as_uint(ent_from_key((uint32_t)(sm.keys[i] >> 32)));
-      if (bits_finite(u)) fx_add(local, fx_from_f32_bits(u));
-    }
-    sm.scan[tid] = local;
-  }
-  __syncthreads();
-  // Inclusive scan of the segment totals (Hillis-Steele; integer adds, so the
-  // order does not change the result).
-  for (int off = 1; off < kScanThreads; off <<= 1) {
-    Fx add;
-    fx_zero(add);
-    if (tid < kScanThreads && tid >= off) add = sm.scan[tid - off];
-    __syncthreads();
-    if (tid < kScanThreads && tid >= off) fx_add(sm.scan[tid], add);
-    __syncthreads();
-  }
-  if (tid < kScanThreads && lo < hi) {
-    Fx s;
-    fx_zero(s);
-    if (tid > 0) s = sm.scan[tid - 1];
-    const int neg_all = *n_neg_all, pos_all = *n_pos_all;
-    for (int i = lo; i < hi; ++i) {
-      const int n_neg = min(i, neg_all);
-      const int n_pos = max(0, i - (nc - pos_all));
-      if (!ent_prefix_ok(r, s, n_neg, n_pos)) {
-        atomicMin(first_fail, i);
-        break;
-      }
-      const uint32_t u = __float_as_uint(ent_from_key((uint32_t)(sm.keys[i] >> 32)));
-      if (bits_finite(u)) fx_add(s, fx_from_f32_bits(u));
-    }
-  }
-  __syncthreads();
-  const int n = nc ? max(*first_fail, 1) : 0;
-  commit_prefix(r, b, L, n, sm);
+  if (tid == 0 && *n_pass == 0 && *best != kSentinel) o_row[(uint32_t)*best] = 1;
 }
 
 // Runs a ranking rule on batch row b.  Every thread of the workgroup must call
@@ -276,12 +443,35 @@ __device__ inline void rule_entropy_bound(const RuleDev &r, int b, int L, const 
 __device__ inline void run_batch_rule(const RuleDev &r, int b, int L, const float *conf,
                                       const float *ent, unsigned char *smem) {
   const RuleSmem sm = rule_smem(smem, L);
+  const bool short_row = L <= (int)blockDim.x;
   switch (r.kind) {
-    case DLLM_RULE_THRESHOLD: rule_threshold(r, b, L, conf, sm); break;
-    case DLLM_RULE_TOPK: rule_topk(r, b, L, conf, sm); break;
-    case DLLM_RULE_FACTOR: rule_factor(r, b, L, conf, sm); break;
-    case DLLM_RULE_ENTROPY_BOUND: rule_entropy_bound(r, b, L, ent, sm); break;
-    default: break;
+    case DLLM_RULE_THRESHOLD:
+      rule_threshold(r, b, L, conf, sm);
+      break;
+    case DLLM_RULE_TOPK:
+    case DLLM_RULE_FACTOR:
+      if (short_row) short_rank_rule(r, b, L, conf, sm);
+      else long_rank_rule(r, b, L, conf, sm);
+      break;
+    case DLLM_RULE_ENTROPY_BOUND: {
+      bool done = false;
+      if (short_row) {
+        // fast path only when every candidate entropy is finite and >= 0
+        // (-0 counts as 0)
+        const int t = threadIdx.x;
+        bool bad = false;
+        if (t < L && r.mask[(int64_t)b * L + t]) {
+          const uint32_t u = __float_as_uint(load_coherent(ent + (int64_t)b * L + t));
+          bad = u != 0x80000000u && (!bits_finite(u) || (u & 0x80000000u) != 0);
+        }
+        if (!__syncthreads_or(bad)) done = short_entropy_rule(r, b, L, ent, sm);
+      }
+      __syncthreads();
+      if (!done) long_entropy_rule(r, b, L, ent, sm);
+      break;
+    }
+    default:
+      break;
   }
   __syncthreads();
 }

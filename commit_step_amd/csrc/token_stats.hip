@@ -56,6 +56,38 @@ struct Partial {          // one row slice's statistics (workspace)
   int pad;
 };
 
+// Publishing to other workgroups of the same launch, which may run on other
+// XCDs (each with its own L2): values are written with agent-scope atomic
+// stores (coherent at device level), the writer waits until they have
+// completed, and only then counts itself in with a device-scope atomic; the
+// reader, having seen the count, reads them with agent-scope atomic loads.
+// This is the mechanism an agent-scope release/acquire uses for atomic data,
+// without the writeback of the whole L2 that non-atomic data would need.
+template <typename V>
+__device__ __forceinline__ void store_coherent(V *p, V v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename V>
+__device__ __forceinline__ V load_coh(const V *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores_complete() { __builtin_amdgcn_s_waitcnt(0); }
+
+__device__ __forceinline__ void store_partial(Partial *dst, const Partial &p) {
+  store_coherent(&dst->M, p.M); store_coherent(&dst->idx, p.idx);
+  store_coherent(&dst->z, p.z); store_coherent(&dst->S, p.S);
+  store_coherent(&dst->sb, p.sb); store_coherent(&dst->ib, p.ib);
+  store_coherent(&dst->xb, p.xb);
+}
+__device__ __forceinline__ Partial load_partial(const Partial *src) {
+  Partial p;
+  p.M = load_coh(&src->M); p.idx = load_coh(&src->idx);
+  p.z = load_coh(&src->z); p.S = load_coh(&src->S);
+  p.sb = load_coh(&src->sb); p.ib = load_coh(&src->ib);
+  p.xb = load_coh(&src->xb); p.pad = 0;
+  return p;
+}
+
 struct StatsArgs {
   const void *logits;
   int64_t row_stride;
@@ -123,17 +155,23 @@ __device__ __forceinline__ float clamp_d(float d) {
   return __uint_as_float(min(__float_as_uint(d), 0xC3480000u));
 }
 
-// Process one chunk of CH elements (x[], with element indices given by idx_of).
-template <int CH, typename IdxF>
-__device__ __forceinline__ void chunk_update(WaveState &st, const float (&x)[CH], IdxF idx_of) {
+// Process one chunk: every lane holds CH = U * VEC elements, element j of load
+// k at index idx_of(k, j, lane).  The wave maximum is taken first; the
+// accumulators are relative to it.
+template <int U, int VEC, typename IdxF>
+__device__ __forceinline__ void chunk_update(WaveState &st, const float (&x)[U * VEC],
+                                             IdxF idx_of) {
+  constexpr int CH = U * VEC;
   float cm = x[0];
 #pragma unroll
   for (int e = 1; e < CH; ++e) cm = fmaxf(cm, x[e]);
   const float cmw = wave_max(cm);
   if (cmw > st.M) {
-    // The wave maximum rises (rare after the first chunks): rescale, demote the
-    // old maximal element into the uniform extra sum, and exclude exactly one
-    // new maximal element from z.
+    // The wave maximum rises (about ln(#chunks) times per wave): rescale,
+    // demote the old maximal element into the uniform extra sum, and exclude
+    // the new maximal elements from z (one of them stays out; the others are
+    // ties and re-enter through zx).  Counting and locating them runs on the
+    // scalar unit from ballots.
     if (st.M != -kInf) {
       const float delta = (st.M - cmw) * kLog2e;
       const float f = __builtin_amdgcn_exp2f(delta);
@@ -146,23 +184,37 @@ __device__ __forceinline__ void chunk_update(WaveState &st, const float (&x)[CH]
     st.M = cmw;
     int cnt = 0, first = kIdxNone;
 #pragma unroll
-    for (int e = 0; e < CH; ++e) {
-      const bool eq = x[e] == cmw;
-      const float d = clamp_d((x[e] - cmw) * kLog2e);
-      const float t = eq ? 0.0f : __builtin_amdgcn_exp2f(d);
-      st.z += t;
-      st.S = fmaf(t, d, st.S);
-      cnt += eq ? 1 : 0;
-      first = (eq && first == kIdxNone) ? idx_of(e) : first;
+    for (int k = 0; k < U; ++k) {
+      uint64_t lanes = 0;
+      uint64_t m[VEC];
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) {
+        const float xv = x[k * VEC + j];
+        const bool eq = xv == cmw;
+        m[j] = __builtin_amdgcn_ballot_w64(eq);
+        cnt += __builtin_popcountll(m[j]);
+        lanes |= m[j];
+        const float d = clamp_d((xv - cmw) * kLog2e);
+        const float t = eq ? 0.0f : __builtin_amdgcn_exp2f(d);
+        st.z += t;
+        st.S = fmaf(t, d, st.S);
+      }
+      if (first == kIdxNone && lanes != 0) {
+        const int ln = __builtin_ctzll(lanes);
+        int jj = 0;
+#pragma unroll
+        for (int j = VEC - 1; j >= 0; --j)
+          if ((m[j] >> ln) & 1ull) jj = j;
+        first = idx_of(k, jj, ln);
+      }
     }
-    const int cnt_w = wave_sum_i(cnt);
-    st.idx = wave_min_i(first);
-    st.zx += (float)(cnt_w - 1);
+    st.idx = first;
+    st.zx += (float)(cnt - 1);
   } else if (st.M != -kInf) {
-    const float m = st.M;
+    const float mm = st.M;
 #pragma unroll
     for (int e = 0; e < CH; ++e) {
-      const float d = clamp_d((x[e] - m) * kLog2e);
+      const float d = clamp_d((x[e] - mm) * kLog2e);
       const float t = __builtin_amdgcn_exp2f(d);
       st.z += t;
       st.S = fmaf(t, d, st.S);
@@ -209,14 +261,16 @@ __device__ __forceinline__ float gumbel_at(const StatsArgs &a, uint32_t b, uint3
 }
 
 // Stream [lo, hi) of one row.  VECLOAD: 16-byte loads (row start 16-byte
-// aligned, lo/hi multiples of VEC).  Returns this workgroup's partial in
-// *out (valid in thread 0).
-template <typename T, int NT, bool SAMPLE, bool VECLOAD>
+// aligned, lo/hi multiples of VEC).  Full workgroup iterations run without
+// bounds checks, with the next iteration's loads in flight while the current
+// one is reduced; one masked iteration finishes the slice.  The workgroup's
+// partial lands in *out (valid in thread 0).
+template <typename T, int NT, int UV, bool SAMPLE, bool VECLOAD>
 __device__ void stream_slice(const StatsArgs &a, const T *row, int64_t lo, int64_t hi,
                              uint32_t b, uint32_t l, Partial *wave_parts, Partial *out) {
   using E = ElemT<T>;
   constexpr int VEC = VECLOAD ? E::VEC : 1;
-  constexpr int U = VECLOAD ? E::U : 8;
+  constexpr int U = VECLOAD ? UV : 8;
   constexpr int CH = VEC * U;
   constexpr int STEP = NT * CH;                 // elements per workgroup iteration
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -224,32 +278,9 @@ __device__ void stream_slice(const StatsArgs &a, const T *row, int64_t lo, int64
   WaveState st;
   st.M = -kInf; st.idx = kIdxNone; st.zx = 0.f; st.Sx = 0.f; st.z = 0.f; st.S = 0.f;
   st.sb = -kInf; st.ib = kIdxNone; st.xb = -kInf;
-
   int sp = 0;   // next suppress id not below the current iteration
-  for (int64_t base = lo; base < hi; base += STEP) {
-    float x[CH];
-    if constexpr (VECLOAD) {
-      uint4 raw[U];
-#pragma unroll
-      for (int k = 0; k < U; ++k) {
-        const int64_t v0 = base + (int64_t)(k * NT + tid) * VEC;
-        if (v0 < hi) raw[k] = *reinterpret_cast<const uint4 *>(row + v0);
-        else raw[k] = make_uint4(0xff80ff80u, 0xff80ff80u, 0xff80ff80u, 0xff80ff80u);
-      }
-#pragma unroll
-      for (int k = 0; k < U; ++k) {
-        const int64_t v0 = base + (int64_t)(k * NT + tid) * VEC;
-#pragma unroll
-        for (int e = 0; e < VEC; ++e)
-          x[k * VEC + e] = (v0 < hi) ? E::at(raw[k], e) : -kInf;
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < U; ++k) {
-        const int64_t v = base + (int64_t)(k * NT + tid);
-        x[k] = (v < hi) ? E::load1(row + v) : -kInf;
-      }
-    }
+
+  auto process = [&](float (&x)[CH], int64_t base) {
     // suppress ids inside this iteration (rare, workgroup-uniform test)
     while (sp < a.n_suppress && a.suppress[sp] < base) ++sp;
     if (sp < a.n_suppress && a.suppress[sp] < base + STEP) {
@@ -264,9 +295,6 @@ __device__ void stream_slice(const StatsArgs &a, const T *row, int64_t lo, int64
         }
       }
     }
-    auto idx_of = [&](int e) -> int {
-      return (int)(base + (int64_t)((e / VEC) * NT + tid) * VEC + (e % VEC));
-    };
     if constexpr (SAMPLE) {
 #pragma unroll
       for (int k = 0; k < U; ++k) {
@@ -279,20 +307,77 @@ __device__ void stream_slice(const StatsArgs &a, const T *row, int64_t lo, int64
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const float xv = x[k * VEC + 4 * q + j];
-              const float s = fmaf(xv, a.inv_temp, gumbel_from_word(p.w[j]));
-              if (s > st.sb) { st.sb = s; st.ib = (int)(vq + j); st.xb = xv; }
+              const float sc = fmaf(xv, a.inv_temp, gumbel_from_word(p.w[j]));
+              if (sc > st.sb) { st.sb = sc; st.ib = (int)(vq + j); st.xb = xv; }
             }
           }
         } else {
           const float xv = x[k];
           if (v0 < hi) {
-            const float s = fmaf(xv, a.inv_temp, gumbel_at(a, b, l, v0));
-            if (s > st.sb) { st.sb = s; st.ib = (int)v0; st.xb = xv; }
+            const float sc = fmaf(xv, a.inv_temp, gumbel_at(a, b, l, v0));
+            if (sc > st.sb) { st.sb = sc; st.ib = (int)v0; st.xb = xv; }
           }
         }
       }
     }
-    chunk_update<CH>(st, x, idx_of);
+    chunk_update<U, VEC>(st, x, [&](int k, int j, int ln) -> int {
+      return (int)(base + (int64_t)(k * NT + wave * 64 + ln) * VEC + j);
+    });
+  };
+
+  float x[CH];
+  if constexpr (VECLOAD) {
+    constexpr int64_t ITER = STEP / VEC;          // uint4 per workgroup iteration
+    const int64_t n_full = (hi - lo) / STEP;
+    const uint4 *p = reinterpret_cast<const uint4 *>(row + lo) + tid;
+    if (n_full > 0) {
+      uint4 nxt[U];
+#pragma unroll
+      for (int k = 0; k < U; ++k) nxt[k] = p[k * NT];
+      for (int64_t it = 0; it + 1 < n_full; ++it) {
+        uint4 cur[U];
+#pragma unroll
+        for (int k = 0; k < U; ++k) cur[k] = nxt[k];
+        const uint4 *q = p + (it + 1) * ITER;
+#pragma unroll
+        for (int k = 0; k < U; ++k) nxt[k] = q[k * NT];
+#pragma unroll
+        for (int k = 0; k < U; ++k)
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) x[k * VEC + e] = E::at(cur[k], e);
+        process(x, lo + it * STEP);
+      }
+#pragma unroll
+      for (int k = 0; k < U; ++k)
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) x[k * VEC + e] = E::at(nxt[k], e);
+      process(x, lo + (n_full - 1) * STEP);
+    }
+    const int64_t tb = lo + n_full * STEP;
+    if (tb < hi) {
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        const int64_t v0 = tb + (int64_t)(k * NT + tid) * VEC;
+        if (v0 < hi) {
+          const uint4 r = *reinterpret_cast<const uint4 *>(row + v0);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) x[k * VEC + e] = E::at(r, e);
+        } else {
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) x[k * VEC + e] = -kInf;
+        }
+      }
+      process(x, tb);
+    }
+  } else {
+    for (int64_t base = lo; base < hi; base += STEP) {
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        const int64_t v = base + (int64_t)(k * NT + tid);
+        x[k] = (v < hi) ? E::load1(row + v) : -kInf;
+      }
+      process(x, base);
+    }
   }
 
   // Wave partial -> LDS.
@@ -430,7 +515,7 @@ __device__ RowResult slow_row(const StatsArgs &a, const T *row, uint32_t b, uint
   return r;
 }
 
-template <typename T, int NT, bool SAMPLE, bool VECLOAD>
+template <typename T, int NT, int UV, bool SAMPLE, bool VECLOAD>
 __global__ __launch_bounds__(NT) void token_stats_kernel(StatsArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];   // rules (dynamic)
   __shared__ Partial wave_parts[NT / 64];
@@ -447,20 +532,20 @@ __global__ __launch_bounds__(NT) void token_stats_kernel(StatsArgs a) {
   const int64_t lo = (int64_t)slice * a.slice_len;
   const int64_t hi = min(lo + a.slice_len, a.V);
 
-  stream_slice<T, NT, SAMPLE, VECLOAD>(a, row, lo, hi, b, l, wave_parts, &slice_parts_acc);
+  stream_slice<T, NT, UV, SAMPLE, VECLOAD>(a, row, lo, hi, b, l, wave_parts, &slice_parts_acc);
 
   // Split rows: publish the slice partial; the last slice to finish merges.
   if (a.slices > 1) {
     if (tid == 0) {
-      a.partials[row_id * a.slices + slice] = slice_parts_acc;
-      __threadfence();
+      // publish the slice partial, count the slice; the last slice merges
+      store_partial(&a.partials[row_id * a.slices + slice], slice_parts_acc);
+      wait_stores_complete();
       const uint32_t prev = atomicAdd(&a.row_count[row_id], 1u);
       s_flag = (prev == (uint32_t)(a.slices - 1));
       if (s_flag) {
-        __threadfence();
-        Partial acc = a.partials[row_id * a.slices];
+        Partial acc = load_partial(&a.partials[row_id * a.slices]);
         for (int s = 1; s < a.slices; ++s) {
-          const Partial q = a.partials[row_id * a.slices + s];
+          const Partial q = load_partial(&a.partials[row_id * a.slices + s]);
           merge_partial(acc, q);
           if (SAMPLE) merge_sample(acc, q);
         }
@@ -499,8 +584,8 @@ __global__ __launch_bounds__(NT) void token_stats_kernel(StatsArgs a) {
 
   if (tid == 0) {
     a.x0[row_id] = res.x0;
-    a.prob[row_id] = res.prob;
-    a.entropy[row_id] = res.ent;
+    store_coherent(&a.prob[row_id], res.prob);       // read by the batch-row rules
+    store_coherent(&a.entropy[row_id], res.ent);
     if (a.has_edit)
       a.edit_out[row_id] = edit_decision(a.edit_mask[row_id], res.x0, a.edit_tokens[row_id],
                                          res.prob, a.edit_tau);
@@ -508,15 +593,15 @@ __global__ __launch_bounds__(NT) void token_stats_kernel(StatsArgs a) {
   if (a.n_rank_rules == 0) return;
 
   // Batch-row rules: the workgroup that completes the batch row runs them.
+  // Thread 0 counts its row in once its statistics are published; the rules
+  // read the others' with coherent loads.
   if (tid == 0) {
-    __threadfence();
+    wait_stores_complete();
     const uint32_t prev = atomicAdd(&a.batch_count[b], 1u);
     s_flag = (prev == (uint32_t)(a.L - 1));
-    if (s_flag) __threadfence();
   }
   __syncthreads();
   if (!s_flag) return;
-  __threadfence();
   for (int r = 0; r < a.n_rank_rules; ++r)
     run_batch_rule(a.rank_rules[r], (int)b, (int)a.L, a.prob, a.entropy, smem);
   if (tid == 0) a.batch_count[b] = 0u;   // leave the workspace zeroed
@@ -540,8 +625,11 @@ Plan make_plan(int dtype, int64_t rows, int64_t V, int64_t row_stride, const voi
   p.vec = ((uintptr_t)logits % 16 == 0) && ((row_stride * esz) % 16 == 0) && (V % vecn == 0);
   const int cus = device_cu_count();
   // Enough waves to cover HBM latency: aim for >= 16 waves per CU.
+  // Enough waves per CU to cover HBM latency: many rows -> 256-thread groups,
+  // a few long rows -> 512-thread groups (measured best on the 256 x 262144
+  // canvas: 8 waves per CU with one 16-byte-load chunk in flight each).
   if (rows >= 4LL * cus || V < 16384) p.nt = 256;
-  else p.nt = 1024;
+  else p.nt = 512;
   p.slices = 1;
   const int64_t wgs = rows;
   if (wgs < cus && V >= 8192) {
@@ -566,18 +654,27 @@ size_t workspace_bytes_for(int64_t B, int64_t L, int slices) {
   return bytes;
 }
 
-template <typename T, int NT>
+template <typename T, int NT, int UV>
 hipError_t launch_t(const Plan &p, const StatsArgs &a, int64_t rows, bool sample, size_t smem,
                     hipStream_t s) {
   dim3 grid((unsigned)(rows * p.slices)), block(NT);
   if (sample) {
-    if (p.vec) token_stats_kernel<T, NT, true, true><<<grid, block, smem, s>>>(a);
-    else token_stats_kernel<T, NT, true, false><<<grid, block, smem, s>>>(a);
+    if (p.vec) token_stats_kernel<T, NT, UV, true, true><<<grid, block, smem, s>>>(a);
+    else token_stats_kernel<T, NT, UV, true, false><<<grid, block, smem, s>>>(a);
   } else {
-    if (p.vec) token_stats_kernel<T, NT, false, true><<<grid, block, smem, s>>>(a);
-    else token_stats_kernel<T, NT, false, false><<<grid, block, smem, s>>>(a);
+    if (p.vec) token_stats_kernel<T, NT, UV, false, true><<<grid, block, smem, s>>>(a);
+    else token_stats_kernel<T, NT, UV, false, false><<<grid, block, smem, s>>>(a);
   }
   return hipGetLastError();
+}
+
+// Dispatch on the plan's (threads, loads per chunk).
+template <typename T>
+hipError_t launch_plan(const Plan &p, const StatsArgs &a, int64_t rows, bool sample, size_t smem,
+                       hipStream_t s) {
+  constexpr int U0 = ElemT<T>::U;
+  if (p.nt == 512) return launch_t<T, 512, U0>(p, a, rows, sample, smem, s);
+  return launch_t<T, 256, U0>(p, a, rows, sample, smem, s);
 }
 
 }  // namespace
@@ -708,15 +805,10 @@ extern "C" int dllm_token_stats(const void *logits, int dtype, int64_t B, int64_
   a.entropy = entropy;
 
   const bool sample = temperature > 0.0f;
-  const size_t smem = a.n_rank_rules ? rule_smem_bytes((int)L) : 0;
+  const size_t smem = a.n_rank_rules ? rule_smem_bytes((int)L, p.nt) : 0;
   hipError_t e;
-  if (dtype == DLLM_BF16) {
-    e = p.nt == 1024 ? launch_t<uint16_t, 1024>(p, a, rows, sample, smem, stream)
-                     : launch_t<uint16_t, 256>(p, a, rows, sample, smem, stream);
-  } else {
-    e = p.nt == 1024 ? launch_t<float, 1024>(p, a, rows, sample, smem, stream)
-                     : launch_t<float, 256>(p, a, rows, sample, smem, stream);
-  }
+  if (dtype == DLLM_BF16) e = launch_plan<uint16_t>(p, a, rows, sample, smem, stream);
+  else e = launch_plan<float>(p, a, rows, sample, smem, stream);
   if (e != hipSuccess)
     return fail(DLLM_ERR_HIP, "dllm_token_stats: launch failed: %s", hipGetErrorString(e));
   return ok();

@@ -178,10 +178,14 @@ static int launch_batch_rule(const dllm_rule &rule, int64_t B, int64_t L, const 
   if (rc != DLLM_OK) return rc;
   if ((const void *)rule.out == (const void *)scores || (const void *)rule.out == (const void *)rule.mask)
     return fail(DLLM_ERR_ARG, "%s: the output aliases an input", who);
-  const size_t smem = rule_smem_bytes((int)L);
-  const int nt = L > 1024 ? 1024 : 256;
+  // one position per thread (the short-row paths) up to 1024 positions
+  const int np = rule_pow2((int)L);
+  const int nt = np > 512 ? 1024 : (np > 256 ? 512 : 256);
+  const size_t smem = rule_smem_bytes((int)L, nt);
   if (nt == 1024)
     batch_rule_kernel<1024><<<dim3((unsigned)B), dim3(1024), smem, s>>>(d, (int)L, scores, scores);
+  else if (nt == 512)
+    batch_rule_kernel<512><<<dim3((unsigned)B), dim3(512), smem, s>>>(d, (int)L, scores, scores);
   else
     batch_rule_kernel<256><<<dim3((unsigned)B), dim3(256), smem, s>>>(d, (int)L, scores, scores);
   return check_launch(who);
