@@ -206,7 +206,8 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": read_traffic(src_hash),
-                     "kernel": "token_stats_kernel<bf16, 1024 threads, greedy, 16-byte loads>",
+                     "kernel": "dllm::token_stats_kernel (bf16, greedy, 16-byte loads) with "
+                               "entropy_bound and edit fused",
                      "algorithmic_bytes_per_launch": alg_bytes},
         "kernel_source_sha256": src_hash,
     }
