@@ -55,6 +55,7 @@ struct Partial {          // one row slice's statistics (workspace)
   float xb;               // sampled: its logit
   int pad;
 };
+static_assert(sizeof(Partial) == 32, "Partial is zeroed as two 16-byte words");
 
 // Publishing to other workgroups of the same launch, which may run on other
 // XCDs (each with its own L2): values are written with agent-scope atomic
@@ -137,27 +138,34 @@ template <> struct ElemT<float> {
   __device__ static float load1(const float *p) { return *p; }
 };
 
-// Wave-local running state.
+// Wave-local running state.  Weights are taken against the reference
+// R = RN(M log2 e): an element x weighs 2^(x log2e - R), its exponent one fma,
+// so x log2 e is never rounded on its own.  The wave partial is converted to
+// weights relative to M itself (2^((x - M) log2 e)) when the stream ends,
+// using the exact residual M log2e - R.
 struct WaveState {
   float M;       // wave-uniform running max
+  float R;       // wave-uniform reference RN(M log2 e)
   int idx;       // wave-uniform first index of M
-  float zx, Sx;  // wave-uniform: demoted maxima and ties of M, relative to M
-  float z, S;    // per lane, relative to M
+  float zx, Sx;  // wave-uniform: demoted maxima and ties of M, against R
+  float z, S;    // per lane, against R
   float sb;      // per lane sampled best
   int ib;
   float xb;
 };
 
 __device__ __forceinline__ float clamp_d(float d) {
-  // d <= 0 always; below -200 (and -inf) the term 2^d is 0 in float32.  An
-  // unsigned min on the bits maps every such d (and -inf) to -200 while leaving
-  // [-200, +0] untouched, so 0 * -inf never arises.  NaN d passes through.
+  // d <= a tiny positive residual; below -200 (and -inf) the term 2^d is 0 in
+  // float32.  An unsigned min on the bits maps every such d (and -inf) to -200
+  // while leaving [-200, +inf) untouched, so 0 * -inf never arises.  NaN d
+  // passes through.
   return __uint_as_float(min(__float_as_uint(d), 0xC3480000u));
 }
 
 // Process one chunk: every lane holds CH = U * VEC elements, element j of load
-// k at index idx_of(k, j, lane).  The wave maximum is taken first; the
-// accumulators are relative to it.
+// k at index idx_of(k, j, lane).  A chunk that raises the wave maximum takes
+// the rescaling path; every other chunk costs one fma, one exp2, one add and
+// one fma per element.
 template <int U, int VEC, typename IdxF>
 __device__ __forceinline__ void chunk_update(WaveState &st, const float (&x)[U * VEC],
                                              IdxF idx_of) {
@@ -165,23 +173,27 @@ __device__ __forceinline__ void chunk_update(WaveState &st, const float (&x)[U *
   float cm = x[0];
 #pragma unroll
   for (int e = 1; e < CH; ++e) cm = fmaxf(cm, x[e]);
-  const float cmw = wave_max(cm);
-  if (cmw > st.M) {
+  if (__builtin_amdgcn_ballot_w64(cm > st.M) != 0) {
     // The wave maximum rises (about ln(#chunks) times per wave): rescale,
-    // demote the old maximal element into the uniform extra sum, and exclude
+    // demote the old maximal element into the uniform extra sums, and exclude
     // the new maximal elements from z (one of them stays out; the others are
     // ties and re-enter through zx).  Counting and locating them runs on the
     // scalar unit from ballots.
+    const float cmw = wave_max(cm);
+    const float Rn = cmw * kLog2e;
     if (st.M != -kInf) {
-      const float delta = (st.M - cmw) * kLog2e;
+      const float delta = st.R - Rn;
       const float f = __builtin_amdgcn_exp2f(delta);
       st.S = f * fmaf(delta, st.z, st.S);
       st.z = st.z * f;
-      const float zx1 = st.zx + 1.0f;
-      st.Sx = f * fmaf(delta, zx1, st.Sx);
+      const float e0 = fmaf(st.M, kLog2e, -st.R);      // exact residual
+      const float w0 = __builtin_amdgcn_exp2f(e0);
+      const float zx1 = st.zx + w0;
+      st.Sx = f * fmaf(delta, zx1, fmaf(w0, e0, st.Sx));
       st.zx = zx1 * f;
     }
     st.M = cmw;
+    st.R = Rn;
     int cnt = 0, first = kIdxNone;
 #pragma unroll
     for (int k = 0; k < U; ++k) {
@@ -194,7 +206,7 @@ __device__ __forceinline__ void chunk_update(WaveState &st, const float (&x)[U *
         m[j] = __builtin_amdgcn_ballot_w64(eq);
         cnt += __builtin_popcountll(m[j]);
         lanes |= m[j];
-        const float d = clamp_d((xv - cmw) * kLog2e);
+        const float d = clamp_d(fmaf(xv, kLog2e, -Rn));
         const float t = eq ? 0.0f : __builtin_amdgcn_exp2f(d);
         st.z += t;
         st.S = fmaf(t, d, st.S);
@@ -209,17 +221,46 @@ __device__ __forceinline__ void chunk_update(WaveState &st, const float (&x)[U *
       }
     }
     st.idx = first;
-    st.zx += (float)(cnt - 1);
+    if (cnt > 1) {
+      // ties of the new maximum weigh 2^e1 against R
+      const float e1 = fmaf(cmw, kLog2e, -Rn);
+      const float w1 = (float)(cnt - 1) * __builtin_amdgcn_exp2f(e1);
+      st.zx += w1;
+      st.Sx = fmaf(w1, e1, st.Sx);
+    }
   } else if (st.M != -kInf) {
-    const float mm = st.M;
+    const float nR = -st.R;
+    const float S0 = st.S;
 #pragma unroll
     for (int e = 0; e < CH; ++e) {
-      const float d = clamp_d((x[e] - mm) * kLog2e);
+      const float d = fmaf(x[e], kLog2e, nR);
       const float t = __builtin_amdgcn_exp2f(d);
       st.z += t;
       st.S = fmaf(t, d, st.S);
     }
+    if (__builtin_amdgcn_ballot_w64(st.S != st.S) != 0) {
+      // a -inf logit made 0 * -inf: redo this chunk's S with clamped exponents
+      // (a NaN logit leaves z NaN and sends the row to the slow path anyway)
+      st.S = S0;
+#pragma unroll
+      for (int e = 0; e < CH; ++e) {
+        const float d = clamp_d(fmaf(x[e], kLog2e, nR));
+        st.S = fmaf(__builtin_amdgcn_exp2f(d), d, st.S);
+      }
+    }
   }
+}
+
+// Wave sums against R -> weights relative to M (exact residual e = M log2e - R:
+// 2^(x log2e - M log2e) = 2^(x log2e - R) 2^-e).  A reference that overflowed
+// (|M| > 2^127 / log2 e) poisons z so the row takes the two-pass path.
+__device__ __forceinline__ void to_max_relative(const WaveState &st, float &z, float &S) {
+  if (st.M == -kInf) return;
+  if (!bits_finite(__float_as_uint(st.R))) { z = __builtin_nanf(""); return; }
+  const float e = fmaf(st.M, kLog2e, -st.R);
+  const float g = __builtin_amdgcn_exp2f(-e);
+  S = g * fmaf(-e, z, S);
+  z = g * z;
 }
 
 // Merge partial b into a (a, b relative to their own maxima).
@@ -276,7 +317,7 @@ __device__ void stream_slice(const StatsArgs &a, const T *row, int64_t lo, int64
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   WaveState st;
-  st.M = -kInf; st.idx = kIdxNone; st.zx = 0.f; st.Sx = 0.f; st.z = 0.f; st.S = 0.f;
+  st.M = -kInf; st.R = -kInf; st.idx = kIdxNone; st.zx = 0.f; st.Sx = 0.f; st.z = 0.f; st.S = 0.f;
   st.sb = -kInf; st.ib = kIdxNone; st.xb = -kInf;
   int sp = 0;   // next suppress id not below the current iteration
 
@@ -330,28 +371,37 @@ __device__ void stream_slice(const StatsArgs &a, const T *row, int64_t lo, int64
     constexpr int64_t ITER = STEP / VEC;          // uint4 per workgroup iteration
     const int64_t n_full = (hi - lo) / STEP;
     const uint4 *p = reinterpret_cast<const uint4 *>(row + lo) + tid;
-    if (n_full > 0) {
-      uint4 nxt[U];
+    // Two register buffers in turn: the loads of iteration i + 1 are in flight
+    // while iteration i is reduced, and no buffer is ever copied.
+    auto load = [&](uint4 (&r)[U], int64_t it) {
+      const uint4 *q = p + it * ITER;
 #pragma unroll
-      for (int k = 0; k < U; ++k) nxt[k] = p[k * NT];
-      for (int64_t it = 0; it + 1 < n_full; ++it) {
-        uint4 cur[U];
-#pragma unroll
-        for (int k = 0; k < U; ++k) cur[k] = nxt[k];
-        const uint4 *q = p + (it + 1) * ITER;
-#pragma unroll
-        for (int k = 0; k < U; ++k) nxt[k] = q[k * NT];
-#pragma unroll
-        for (int k = 0; k < U; ++k)
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) x[k * VEC + e] = E::at(cur[k], e);
-        process(x, lo + it * STEP);
-      }
+      for (int k = 0; k < U; ++k) r[k] = q[k * NT];
+    };
+    auto run = [&](const uint4 (&r)[U], int64_t it) {
 #pragma unroll
       for (int k = 0; k < U; ++k)
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) x[k * VEC + e] = E::at(nxt[k], e);
-      process(x, lo + (n_full - 1) * STEP);
+        for (int e = 0; e < VEC; ++e) x[k * VEC + e] = E::at(r[k], e);
+      process(x, lo + it * STEP);
+    };
+    if (n_full > 0) {
+      uint4 ba[U], bb[U];
+      load(ba, 0);
+      int64_t it = 0;
+      for (; it + 2 < n_full; it += 2) {
+        load(bb, it + 1);
+        run(ba, it);
+        load(ba, it + 2);
+        run(bb, it + 1);
+      }
+      if (it + 1 < n_full) {
+        load(bb, it + 1);
+        run(ba, it);
+        run(bb, it + 1);
+      } else {
+        run(ba, it);
+      }
     }
     const int64_t tb = lo + n_full * STEP;
     if (tb < hi) {
@@ -386,6 +436,7 @@ __device__ void stream_slice(const StatsArgs &a, const T *row, int64_t lo, int64
   p.idx = st.idx;
   p.z = wave_sum(st.z) + st.zx;
   p.S = wave_sum(st.S) + st.Sx;
+  to_max_relative(st, p.z, p.S);
   p.sb = -kInf; p.ib = kIdxNone; p.xb = -kInf; p.pad = 0;
   if constexpr (SAMPLE) {
     // first-best over the lanes: max score, lowest index on ties
@@ -543,14 +594,22 @@ __global__ __launch_bounds__(NT) void token_stats_kernel(StatsArgs a) {
       const uint32_t prev = atomicAdd(&a.row_count[row_id], 1u);
       s_flag = (prev == (uint32_t)(a.slices - 1));
       if (s_flag) {
-        Partial acc = load_partial(&a.partials[row_id * a.slices]);
+        Partial *parts = &a.partials[row_id * a.slices];
+        Partial acc = load_partial(&parts[0]);
         for (int s = 1; s < a.slices; ++s) {
-          const Partial q = load_partial(&a.partials[row_id * a.slices + s]);
+          const Partial q = load_partial(&parts[s]);
           merge_partial(acc, q);
           if (SAMPLE) merge_sample(acc, q);
         }
         slice_parts_acc = acc;
-        a.row_count[row_id] = 0u;       // leave the workspace zeroed
+        // Leave the workspace zero-filled: the counter and the partials (a
+        // later call of another shape may lay its counters over them).
+        for (int s = 0; s < a.slices; ++s) {
+          uint4 *w = reinterpret_cast<uint4 *>(&parts[s]);
+          w[0] = make_uint4(0u, 0u, 0u, 0u);
+          w[1] = make_uint4(0u, 0u, 0u, 0u);
+        }
+        a.row_count[row_id] = 0u;
       }
     }
     __syncthreads();

@@ -114,6 +114,74 @@ def test_nan_and_inf_rows(dtype, T):
             assert_sampled_x0(gpu[0], ref.x0, arr, dtype, T, 7, 1, sup, pos, "special sampled")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_sparse_minus_inf_logits(dtype):
+    """Masked vocabulary entries (-inf) scattered through otherwise finite rows,
+    also next to a rising maximum: the fast path must keep every row finite."""
+    rng = np.random.default_rng(21)
+    B, L, V = 2, 12, 40000
+    x = (rng.standard_normal((B, L, V)) * 3).astype(np.float32)
+    x[rng.random((B, L, V)) < 0.01] = -np.inf
+    for l in range(L):                     # -inf right beside rising maxima
+        for k in range(1, 6):
+            p = (k * 7001 + 13 * l) % (V - 1)
+            x[0, l, p] = 8.0 + k + l
+            x[0, l, p + 1] = -np.inf
+    x[1, :, : V // 3] = -np.inf            # long masked prefix, then finite
+    arr = bf16_bits(x) if dtype == "bf16" else x
+    log(f"sparse -inf {dtype}")
+    gpu = stats_np(dc.token_stats(to_dev(arr, dtype)))
+    ref = oracle.token_stats(arr, dtype)
+    assert_stats(gpu, ref, dtype, f"sparse -inf {dtype}")
+    assert np.all(np.isfinite(gpu[1])) and np.all(np.isfinite(gpu[2]))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_large_magnitude_logits(dtype):
+    """Offsets and scales far from unit logits: weights are taken against
+    RN(M log2 e) and converted back exactly; beyond |M| log2 e > FLT_MAX the
+    row takes the two-pass path."""
+    rng = np.random.default_rng(22)
+    V = 20000
+    base = rng.standard_normal(V).astype(np.float32)
+    rows = [base * 2 + 3.0e4, base * 2 - 3.0e4, base * 3 + 1.0e6, base * 0.5 - 7.7e5,
+            base * 1e35 + 1e37, np.float32(2.9e38) + base * 1e36,
+            np.full(V, 3.0e38, np.float32) - np.abs(base) * 1e37, base * 1e36 - 3.0e38]
+    x = np.stack([np.clip(r, -3.3e38, 3.3e38) for r in rows]).astype(np.float32)[None]
+    arr = bf16_bits(x) if dtype == "bf16" else x
+    log(f"large magnitudes {dtype}")
+    gpu = stats_np(dc.token_stats(to_dev(arr, dtype)))
+    ref = oracle.token_stats(arr, dtype)
+    assert_stats(gpu, ref, dtype, f"large {dtype}")
+
+
+def test_workspace_left_zero_filled_across_shapes():
+    """The header's workspace contract: every call leaves the workspace
+    zero-filled, so a later call of another shape (whose counters may lie where
+    the first call's split-row partials were) starts clean."""
+    shapes = [(1, 3, 262144), (2, 40, 30000), (1, 70, 65536), (3, 5, 9000)]
+    need = 0
+    for (B, L, V) in shapes:
+        need = max(need, int(dc.load_library().dllm_token_stats_workspace_size(dc.DLLM_BF16, B, L, V)))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for rep in range(2):
+        for i, (B, L, V) in enumerate(shapes):
+            bits, rng = random_logits(300 + i, B, L, V, "bf16", 2.0, 0.5, 5.0, 12.0)
+            cand = torch.from_numpy(rng.random((B, L)) < 0.5).cuda()
+            r = dc.Rule.entropy_bound(cand, 0.5)
+            log(f"workspace reuse {B}x{L}x{V} pass {rep}")
+            st = dc.token_stats(to_dev(bits, "bf16"), temperature=0.7 if rep else 0.0, seed=5,
+                                rules=[r], workspace=ws)
+            torch.cuda.synchronize()
+            assert int(torch.count_nonzero(ws)) == 0, f"workspace dirty after {B}x{L}x{V}"
+            ref = oracle.token_stats(bits, "bf16", temperature=0.7 if rep else 0.0, seed=5)
+            gpu = stats_np(st)
+            if rep == 0:
+                assert_stats(gpu, ref, "bf16", f"reuse {B}x{L}x{V}")
+            eb = oracle.entropy_bound_transfer(gpu[2], cand.cpu().numpy(), 0.5)
+            assert np.array_equal(r.out.cpu().numpy(), eb)
+
+
 def test_suppressed_argmax_and_many_ids():
     rng = np.random.default_rng(4)
     B, L, V = 2, 6, 70000
