@@ -83,6 +83,25 @@ __device__ __forceinline__ int wave_min_i(int v) {
   return __builtin_amdgcn_readlane(v, 63);
 }
 
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  int x = (int)v;
+  x = (int)min((uint32_t)x, (uint32_t)dpp_i<kQuadSwap1>(x, x));
+  x = (int)min((uint32_t)x, (uint32_t)dpp_i<kQuadSwap2>(x, x));
+  x = (int)min((uint32_t)x, (uint32_t)dpp_i<kRowHalfMirror>(x, x));
+  x = (int)min((uint32_t)x, (uint32_t)dpp_i<kRowMirror>(x, x));
+  x = (int)min((uint32_t)x, (uint32_t)dpp_i<kRowBcast15, 0xA>(-1, x));
+  x = (int)min((uint32_t)x, (uint32_t)dpp_i<kRowBcast31, 0xC>(-1, x));
+  return (uint32_t)__builtin_amdgcn_readlane(x, 63);
+}
+
+// Wave minimum of a 64-bit key: the high words first, then the low words of
+// the lanes holding that high word.
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
+  const uint32_t hi = wave_min_u32((uint32_t)(v >> 32));
+  const uint32_t lo = wave_min_u32((uint32_t)(v >> 32) == hi ? (uint32_t)v : 0xffffffffu);
+  return ((uint64_t)hi << 32) | lo;
+}
+
 // ---------------------------------------------------------------- float helpers
 
 __device__ __host__ __forceinline__ bool bits_finite(uint32_t u) {

@@ -62,9 +62,9 @@ __host__ __device__ inline size_t rule_smem_bytes(int L, int nt) {
 struct RuleSmem {
   uint64_t *keys;     // [Np] sorted keys (long rows) / compacted list (short rows)
   double *hs;         // [Np] values matching the list (short rows)
-  double *part_sum;   // [nt] (also the query keys of block_rank)
+  double *part_sum;   // [nt]
   int *part_cnt;      // [nt]
-  int *misc;          // [64]
+  int *misc;          // [128]
 };
 
 __device__ inline RuleSmem rule_smem(unsigned char *base, int L) {
@@ -138,68 +138,75 @@ __device__ inline int exact_first_fail(const RuleDev &r, const float *h, int n, 
 }
 
 // ---------------------------------------------------------------- short rows
+// One position per thread.  Per-wave counts and minima go through LDS slots,
+// one slot per wave (misc ints [0,16) [16,32) [32,48) [48,64), 64-bit slots
+// from int 64 on), so no slot needs clearing first and every phase ends in a
+// single barrier.
 
 __device__ __forceinline__ int lane_prefix(uint64_t m) {   // set bits below this lane
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
 }
 
-// Appends the `pred` threads' values to list[] in thread order and returns the
-// count.  Every thread must call it (wcnt: 16 ints of LDS).
-template <typename V>
-__device__ inline int block_compact(bool pred, V val, V *list, int *wcnt) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  const uint64_t m = __builtin_amdgcn_ballot_w64(pred);
-  if (lane == 0) wcnt[wave] = __builtin_popcountll(m);
-  __syncthreads();
-  int off = 0, total = 0;
-  for (int w = 0; w < nw; ++w) {
-    const int c = wcnt[w];
-    off += w < wave ? c : 0;
-    total += c;
+// Number of list entries in [j0, j1) below q and, with VALS, the sum of their
+// values.  The bounds are wave-uniform, so every lane reads the same entries
+// (broadcast LDS reads); four entries per step, two accumulators.
+template <bool VALS>
+__device__ __forceinline__ void count_below(uint64_t q, const uint64_t *keys, const double *vals,
+                                            int j0, int j1, int &cnt, double &sum) {
+  int c0 = 0, c1 = 0;
+  double s0 = 0.0, s1 = 0.0;
+  int j = j0;
+  for (; j + 4 <= j1; j += 4) {
+    const uint64_t k0 = keys[j], k1 = keys[j + 1], k2 = keys[j + 2], k3 = keys[j + 3];
+    const bool l0 = k0 < q, l1 = k1 < q, l2 = k2 < q, l3 = k3 < q;
+    c0 += (int)l0 + (int)l2;
+    c1 += (int)l1 + (int)l3;
+    if constexpr (VALS) {
+      const double v0 = vals[j], v1 = vals[j + 1], v2 = vals[j + 2], v3 = vals[j + 3];
+      s0 += l0 ? v0 : 0.0;
+      s1 += l1 ? v1 : 0.0;
+      s0 += l2 ? v2 : 0.0;
+      s1 += l3 ? v3 : 0.0;
+    }
   }
-  if (pred) list[off + lane_prefix(m)] = val;
-  __syncthreads();
-  return total;
+  for (; j < j1; ++j) {
+    const bool lt = keys[j] < q;
+    c0 += (int)lt;
+    if constexpr (VALS) s0 += lt ? vals[j] : 0.0;
+  }
+  cnt = c0 + c1;
+  sum = s0 + s1;
 }
 
-// For the query keys q (thread i < nq holds query i), the number of list keys
-// below the query and the float64 sum of their values (when vals is given).
-// G = blockDim.x / P threads share a query, each counting one part of the
-// list; the owner (thread i < P) returns the totals.  Requires nq <= P.
-__device__ inline int block_rank(uint64_t q, int nq, const uint64_t *list, int n,
-                                 const double *vals, double *sum, const RuleSmem &sm, int P) {
+// Ranks against list[0, n) of nq queries: query i is list[i] for i < n0 and
+// `extra` for i == n0 < nq.  G = blockDim.x / P threads share a query (P a
+// power of two >= max(nq, 64), so each wave works on one part of the list);
+// the owner, thread i < P, returns the count, the value sum and its query.
+template <bool VALS>
+__device__ inline int block_rank(int nq, int n0, uint64_t extra, const uint64_t *list, int n,
+                                 const double *vals, const RuleSmem &sm, int P, double &sum,
+                                 uint64_t &query) {
   const int t = threadIdx.x, G = blockDim.x / P, part = t / P, i = t - part * P;
   const int per = (n + G - 1) / G;
   const int j0 = min(part * per, n), j1 = min(j0 + per, n);
-  uint64_t *qk = reinterpret_cast<uint64_t *>(sm.part_sum);
-  if (G > 1) {
-    if (part == 0 && i < nq) qk[i] = q;
-    __syncthreads();
-  }
-  const uint64_t myq = G > 1 ? (i < nq ? qk[i] : kSentinel) : q;
-  if (G > 1) __syncthreads();
+  const uint64_t q = i < n0 ? list[i] : (i < nq ? extra : kSentinel);
   int cnt = 0;
   double s = 0.0;
-  if (i < nq) {
-    if (vals) {
-      for (int j = j0; j < j1; ++j) {
-        const bool lt = list[j] < myq;
-        cnt += lt;
-        s += lt ? vals[j] : 0.0;
-      }
-    } else {
-#pragma unroll 4
-      for (int j = j0; j < j1; ++j) cnt += list[j] < myq;
-    }
-  }
+  if (i < nq) count_below<VALS>(q, list, vals, j0, j1, cnt, s);
   if (G > 1) {
-    if (part > 0 && i < nq) { sm.part_cnt[t] = cnt; sm.part_sum[t] = s; }
+    if (part > 0 && i < nq) {
+      sm.part_cnt[t] = cnt;
+      if (VALS) sm.part_sum[t] = s;
+    }
     __syncthreads();
     if (part == 0 && i < nq)
-      for (int g = 1; g < G; ++g) { cnt += sm.part_cnt[g * P + i]; s += sm.part_sum[g * P + i]; }
-    __syncthreads();
+      for (int g = 1; g < G; ++g) {
+        cnt += sm.part_cnt[g * P + i];
+        if (VALS) s += sm.part_sum[g * P + i];
+      }
   }
-  if (sum) *sum = s;
+  sum = s;
+  query = q;
   return cnt;
 }
 
@@ -209,90 +216,143 @@ __device__ __forceinline__ int owners_for(int n, int nt) {
   return P < nt ? P : nt;
 }
 
+// Sum over the waves' slots, and the part of it from waves below `wave`.
+__device__ __forceinline__ int slots_sum(const int *slots, int nw, int wave, int *below) {
+  int tot = 0, lo = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int c = slots[w];
+    lo += w < wave ? c : 0;
+    tot += c;
+  }
+  if (below) *below = lo;
+  return tot;
+}
+
 // topk / factor on a short row.
 __device__ inline void short_rank_rule(const RuleDev &r, int b, int L, const float *conf,
                                        const RuleSmem &sm) {
-  const int t = threadIdx.x;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, nw = blockDim.x >> 6;
   const uint8_t *m_row = r.mask + (int64_t)b * L;
   uint8_t *o_row = r.out + (int64_t)b * L;
   const bool cand = t < L && m_row[t];
   const float c = cand ? conf_sanitized(load_coherent(conf + (int64_t)b * L + t)) : 0.f;
   const uint64_t key = cand ? (((uint64_t)conf_key(c) << 32) | (uint32_t)t) : kSentinel;
-  int *ff = sm.misc + 20;
-  if (t == 0) *ff = 0x7fffffff;
-  const int n = block_compact(cand, key, sm.keys, sm.misc);
+  int *wcnt = sm.misc, *wfail = sm.misc + 32;
+  const uint64_t m = __builtin_amdgcn_ballot_w64(cand);
+  if (lane == 0) wcnt[wave] = __builtin_popcountll(m);
+  __syncthreads();
+  int off;
+  const int n = slots_sum(wcnt, nw, wave, &off);
+  if (cand) sm.keys[off + lane_prefix(m)] = key;
+  __syncthreads();
   const int P = owners_for(n, blockDim.x);
-  const uint64_t q = t < n ? sm.keys[t] : kSentinel;
-  const int rank = block_rank(q, n, sm.keys, n, nullptr, nullptr, sm, P);
+  double unused;
+  uint64_t q;
+  const int rank = block_rank<false>(n, n, kSentinel, sm.keys, n, nullptr, sm, P, unused, q);
+  const bool owner = t < n;     // thread t < n owns query t
   int n_commit;
   if (r.kind == DLLM_RULE_TOPK) {
     const int k = r.k[b];
     n_commit = k < 0 ? 0 : (k > n ? n : k);
   } else {
-    if (t < n && !factor_holds(rank, conf_from_key((uint32_t)(q >> 32)), r.param)) atomicMin(ff, rank);
+    const bool fails = owner && !factor_holds(rank, conf_from_key((uint32_t)(q >> 32)), r.param);
+    const int wmin = wave_min_i(fails ? rank : 0x7fffffff);
+    if (lane == 0) wfail[wave] = wmin;
     __syncthreads();
-    const int first = *ff;
+    int first = 0x7fffffff;
+    for (int w = 0; w < nw; ++w) first = min(first, wfail[w]);
     n_commit = n ? max(first < n ? first : n, 1) : 0;
   }
-  if (t < n) o_row[(uint32_t)q] = rank < n_commit ? 1 : 0;
-  if (t < L && !m_row[t]) o_row[t] = 0;
+  if (owner) o_row[(uint32_t)q] = rank < n_commit ? 1 : 0;
+  if (t < L && !cand) o_row[t] = 0;
 }
 
-// entropy_bound on a short row whose candidate entropies are all finite and
-// >= 0.  Returns false (nothing written) when the subset H <= gamma is too
-// large for the all-pairs pass; the caller then takes the sorted path.
+// entropy_bound on a short row.  Returns false (nothing written, every thread
+// alike) when a candidate entropy is negative or not finite, or the subset
+// H <= gamma is too large for the all-pairs pass; the caller then takes the
+// sorted path.  Entropies being >= 0, only candidates with H <= gamma can be
+// followed by another committed one, so ranks and prefix sums run over that
+// subset F plus the smallest key above gamma.
 __device__ inline bool short_entropy_rule(const RuleDev &r, int b, int L, const float *ent,
                                           const RuleSmem &sm) {
-  const int t = threadIdx.x, nt = blockDim.x;
+  const int t = threadIdx.x, nt = blockDim.x, lane = t & 63, wave = t >> 6, nw = nt >> 6;
   const uint8_t *m_row = r.mask + (int64_t)b * L;
   uint8_t *o_row = r.out + (int64_t)b * L;
   const bool cand = t < L && m_row[t];
   const float h = cand ? load_coherent(ent + (int64_t)b * L + t) : 0.f;
+  const uint32_t u = __float_as_uint(h);
+  const bool bad = cand && u != 0x80000000u && (!bits_finite(u) || (u & 0x80000000u) != 0);
   const uint64_t key = cand ? (((uint64_t)ent_key(h) << 32) | (uint32_t)t) : kSentinel;
   const bool in_f = cand && (double)h <= r.param;
-  unsigned long long *next = reinterpret_cast<unsigned long long *>(sm.misc + 24);
-  int *ff = sm.misc + 20;
-  int *slot = sm.misc + 22;
-  if (t == 0) { *next = kSentinel; *ff = 0x7fffffff; }
+  const bool above = cand && !in_f;
+  int *wF = sm.misc, *wA = sm.misc + 16, *wFail = sm.misc + 32, *wUnc = sm.misc + 48;
+  uint64_t *wNext = reinterpret_cast<uint64_t *>(sm.misc + 64);
+  int *slot = sm.misc + 100;
+  const uint64_t mF = __builtin_amdgcn_ballot_w64(in_f);
+  const uint64_t mA = __builtin_amdgcn_ballot_w64(above);
+  const bool wbad = __builtin_amdgcn_ballot_w64(bad) != 0;
+  const uint64_t wnext = wave_min_u64(above ? key : kSentinel);
+  if (lane == 0) {
+    wF[wave] = __builtin_popcountll(mF);
+    wA[wave] = __builtin_popcountll(mA) | (wbad ? 0x100000 : 0);
+    wNext[wave] = wnext;
+  }
   __syncthreads();
-  // the smallest key among the candidates above gamma
-  if (cand && !in_f) atomicMin(next, (unsigned long long)key);
-  const int nF = block_compact(in_f, key, sm.keys, sm.misc);
-  const uint64_t nxt = *next;
-  const int nc = nF + (int)__syncthreads_count(cand && !in_f);
-  if (nF + 1 > nt || nF > 1024) return false;
-  if (t < nF) sm.hs[t] = (double)ent_from_key((uint32_t)(sm.keys[t] >> 32));
+  int offF, nA = 0, anybad = 0;
+  const int nF = slots_sum(wF, nw, wave, &offF);
+  uint64_t nxt = kSentinel;
+  for (int w = 0; w < nw; ++w) {
+    nA += wA[w] & 0xfffff;
+    anybad |= wA[w] >> 20;
+    nxt = wNext[w] < nxt ? wNext[w] : nxt;
+  }
+  if (anybad || nF + 1 > nt || nF > 1024) return false;
+  const int nc = nF + nA;
+  if (in_f) {
+    const int pos = offF + lane_prefix(mF);
+    sm.keys[pos] = key;
+    sm.hs[pos] = (double)h;
+  }
   __syncthreads();
   // queries: every key of F, then the smallest key above gamma (index nF)
   const bool has_next = nxt != kSentinel;
   const int nq = nF + (has_next ? 1 : 0);
-  const uint64_t q = t < nF ? sm.keys[t] : (t == nF && has_next ? nxt : kSentinel);
   const int P = owners_for(nq, nt);
-  double S = 0.0;
-  const int rank = block_rank(q, nq, sm.keys, nF, sm.hs, &S, sm, P);
+  double S;
+  uint64_t q;
+  const int rank = block_rank<true>(nq, nF, nxt, sm.keys, nF, sm.hs, sm, P, S, q);
+  const bool live = t < nq;     // thread t < nq owns query t
   // Entropies are >= 0, so sum |h| = S: |S - exact| <= (terms + 64) 2^-53 S
   // whatever the summation order.
   const double err = (double)(nF + 64) * 0x1p-52 * S;
-  const bool live = t < nq;
   const bool uncertain = live && r.gamma_class == 0 && err != 0.0 && fabs(S - r.param) <= err;
-  bool fails = live && !ent_prefix_ok(r, S <= r.param, 0, 0);
-  if (__syncthreads_count(uncertain)) {
+  const bool fails = live && !ent_prefix_ok(r, S <= r.param, 0, 0);
+  const int wmin = wave_min_i(fails ? rank : 0x7fffffff);
+  const bool wunc = __builtin_amdgcn_ballot_w64(uncertain) != 0;
+  if (lane == 0) {
+    wFail[wave] = wmin;
+    wUnc[wave] = wunc ? 1 : 0;
+  }
+  __syncthreads();
+  int first = 0x7fffffff, anyunc = 0;
+  for (int w = 0; w < nw; ++w) {
+    first = min(first, wFail[w]);
+    anyunc |= wUnc[w];
+  }
+  if (anyunc) {
     // rare: decide the prefixes exactly, in rank order
     float *hsorted = reinterpret_cast<float *>(sm.part_cnt);
     if (live) hsorted[rank] = ent_from_key((uint32_t)(q >> 32));
     __syncthreads();
     const int upto = exact_first_fail(r, hsorted, nq, slot);
-    fails = live && !ent_prefix_ok(r, rank < upto, 0, 0);
+    first = upto < nq ? upto : 0x7fffffff;
   }
-  if (fails) atomicMin(ff, rank);
-  __syncthreads();
-  const int first = *ff;
   // No failure up to the smallest entropy above gamma: the candidate after it
   // fails (its prefix holds an entropy above gamma), or the row ends.
   const int n_star = first != 0x7fffffff ? first : min(nF + 1, nc);
   const int n_commit = nc ? max(n_star, 1) : 0;
   if (live) o_row[(uint32_t)q] = rank < n_commit ? 1 : 0;
-  if (t < L && cand && !in_f && key != nxt) o_row[t] = 0;
+  if (above && key != nxt) o_row[t] = 0;
   if (t < L && !cand) o_row[t] = 0;
   return true;
 }
@@ -454,20 +514,11 @@ __device__ inline void run_batch_rule(const RuleDev &r, int b, int L, const floa
       else long_rank_rule(r, b, L, conf, sm);
       break;
     case DLLM_RULE_ENTROPY_BOUND: {
-      bool done = false;
-      if (short_row) {
-        // fast path only when every candidate entropy is finite and >= 0
-        // (-0 counts as 0)
-        const int t = threadIdx.x;
-        bool bad = false;
-        if (t < L && r.mask[(int64_t)b * L + t]) {
-          const uint32_t u = __float_as_uint(load_coherent(ent + (int64_t)b * L + t));
-          bad = u != 0x80000000u && (!bits_finite(u) || (u & 0x80000000u) != 0);
-        }
-        if (!__syncthreads_or(bad)) done = short_entropy_rule(r, b, L, ent, sm);
+      const bool done = short_row && short_entropy_rule(r, b, L, ent, sm);
+      if (!done) {
+        __syncthreads();
+        long_entropy_rule(r, b, L, ent, sm);
       }
-      __syncthreads();
-      if (!done) long_entropy_rule(r, b, L, ent, sm);
       break;
     }
     default:

@@ -166,7 +166,33 @@ __device__ __forceinline__ float clamp_d(float d) {
 // k at index idx_of(k, j, lane).  A chunk that raises the wave maximum takes
 // the rescaling path; every other chunk costs one fma, one exp2, one add and
 // one fma per element.
+// Lowest index in the chunk of an element equal to v (some lane holds one):
+// the first load k with a match, its lowest lane, that lane's lowest element.
 template <int U, int VEC, typename IdxF>
+__device__ __forceinline__ int first_index_of(const float (&x)[U * VEC], float v, IdxF idx_of) {
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+    uint64_t m[VEC], lanes = 0;
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) {
+      m[j] = __builtin_amdgcn_ballot_w64(x[k * VEC + j] == v);
+      lanes |= m[j];
+    }
+    if (lanes != 0) {
+      const int ln = __builtin_ctzll(lanes);
+      int jj = 0;
+#pragma unroll
+      for (int j = VEC - 1; j >= 0; --j)
+        if ((m[j] >> ln) & 1ull) jj = j;
+      return idx_of(k, jj, ln);
+    }
+  }
+  return kIdxNone;
+}
+
+// ANY_ORDER: chunks may arrive in any index order, so a chunk that ties the
+// maximum can still hold its first occurrence.
+template <int U, int VEC, bool ANY_ORDER, typename IdxF>
 __device__ __forceinline__ void chunk_update(WaveState &st, const float (&x)[U * VEC],
                                              IdxF idx_of) {
   constexpr int CH = U * VEC;
@@ -248,6 +274,10 @@ __device__ __forceinline__ void chunk_update(WaveState &st, const float (&x)[U *
         st.S = fmaf(__builtin_amdgcn_exp2f(d), d, st.S);
       }
     }
+    if constexpr (ANY_ORDER) {
+      if (__builtin_amdgcn_ballot_w64(cm == st.M) != 0)
+        st.idx = min(st.idx, first_index_of<U, VEC>(x, st.M, idx_of));
+    }
   }
 }
 
@@ -319,10 +349,18 @@ __device__ void stream_slice(const StatsArgs &a, const T *row, int64_t lo, int64
   WaveState st;
   st.M = -kInf; st.R = -kInf; st.idx = kIdxNone; st.zx = 0.f; st.Sx = 0.f; st.z = 0.f; st.S = 0.f;
   st.sb = -kInf; st.ib = kIdxNone; st.xb = -kInf;
-  int sp = 0;   // next suppress id not below the current iteration
+  // Greedy rows sweep their full iterations starting at a row-dependent one
+  // (rows lie a power of two apart, and rows swept in lockstep would all
+  // press on the same HBM channels); the sampled path keeps index order.
+  constexpr bool ROTATE = VECLOAD && !SAMPLE;
+  int sp = 0;          // next suppress id not below the current iteration
+  int64_t sp_base = lo;
 
   auto process = [&](float (&x)[CH], int64_t base) {
-    // suppress ids inside this iteration (rare, workgroup-uniform test)
+    // suppress ids inside this iteration (rare, workgroup-uniform test); the
+    // bases ascend except where a rotated sweep wraps around
+    if (base < sp_base) sp = 0;
+    sp_base = base;
     while (sp < a.n_suppress && a.suppress[sp] < base) ++sp;
     if (sp < a.n_suppress && a.suppress[sp] < base + STEP) {
       for (int q = sp; q < a.n_suppress && a.suppress[q] < base + STEP; ++q) {
@@ -361,7 +399,7 @@ __device__ void stream_slice(const StatsArgs &a, const T *row, int64_t lo, int64
         }
       }
     }
-    chunk_update<U, VEC>(st, x, [&](int k, int j, int ln) -> int {
+    chunk_update<U, VEC, ROTATE>(st, x, [&](int k, int j, int ln) -> int {
       return (int)(base + (int64_t)(k * NT + wave * 64 + ln) * VEC + j);
     });
   };
@@ -373,12 +411,19 @@ __device__ void stream_slice(const StatsArgs &a, const T *row, int64_t lo, int64
     const uint4 *p = reinterpret_cast<const uint4 *>(row + lo) + tid;
     // Two register buffers in turn: the loads of iteration i + 1 are in flight
     // while iteration i is reduced, and no buffer is ever copied.
+    const int64_t it0 = (ROTATE && n_full > 1) ? ((int64_t)b * a.L + l) % n_full : 0;
+    auto rot = [&](int64_t it) {
+      const int64_t j = it + it0;
+      return j >= n_full ? j - n_full : j;
+    };
     auto load = [&](uint4 (&r)[U], int64_t it) {
+      it = rot(it);
       const uint4 *q = p + it * ITER;
 #pragma unroll
       for (int k = 0; k < U; ++k) r[k] = q[k * NT];
     };
     auto run = [&](const uint4 (&r)[U], int64_t it) {
+      it = rot(it);
 #pragma unroll
       for (int k = 0; k < U; ++k)
 #pragma unroll

@@ -80,6 +80,27 @@ def test_exact_ties_at_the_maximum():
         assert_stats(gpu, ref, dtype, f"ties {dtype}")
 
 
+def test_rotated_sweeps_keep_first_maximum_and_suppression():
+    """Greedy rows are swept starting at a row-dependent iteration: the first
+    occurrence of a tied maximum must still win wherever the sweep starts, and
+    suppressed ids must be honoured in iterations visited after the wrap."""
+    rng = np.random.default_rng(23)
+    B, L, V = 1, 300, 65536
+    x = np.round(rng.standard_normal((B, L, V)) * 2).astype(np.float32)
+    sup = tuple(sorted({5, 100, 16390, 33000, 49200, 65535}))
+    for l in range(L):
+        pos = rng.choice(V, size=2 + l % 3, replace=False)   # tied maxima across iterations
+        x[0, l, pos] = 20.0
+        x[0, l, sup[l % len(sup)]] = 40.0                     # suppressed raw argmax
+    bits = bf16_bits(x)
+    log("rotated sweeps: ties and suppression")
+    gpu = stats_np(dc.token_stats(to_dev(bits, "bf16"), suppress_ids=sup))
+    ref = oracle.token_stats(bits, "bf16", suppress_ids=sup)
+    assert_stats(gpu, ref, "bf16", "rotated sweeps")
+    f32 = stats_np(dc.token_stats(to_dev(x), suppress_ids=sup))
+    assert_stats(f32, oracle.token_stats(x, "f32", suppress_ids=sup), "f32", "rotated sweeps f32")
+
+
 def _special_rows(V):
     rows = []
     r = np.random.default_rng(3).standard_normal(V).astype(np.float32)
