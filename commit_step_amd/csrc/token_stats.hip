@@ -118,6 +118,14 @@ struct StatsArgs {
   Partial *partials;       // [B*L*slices] (slices > 1)
 };
 
+// Logits are read exactly once: 16-byte loads with the non-temporal hint, so
+// the stream does not churn L2 and the Infinity Cache.
+__device__ __forceinline__ uint4 load_stream(const uint4 *p) {
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 template <typename T> struct ElemT;
 template <> struct ElemT<uint16_t> {   // bf16 bit patterns
   static constexpr int VEC = 8;        // elements per 16-byte load
@@ -164,8 +172,8 @@ __device__ __forceinline__ float clamp_d(float d) {
 
 // Process one chunk: every lane holds CH = U * VEC elements, element j of load
 // k at index idx_of(k, j, lane).  A chunk that raises the wave maximum takes
-// the rescaling path; every other chunk costs one fma, one exp2, one add and
-// one fma per element.
+// the rescaling path; every other chunk costs one fma, one clamp, one exp2,
+// one add and one fma per element.
 // Lowest index in the chunk of an element equal to v (some lane holds one):
 // the first load k with a match, its lowest lane, that lane's lowest element.
 template <int U, int VEC, typename IdxF>
@@ -256,23 +264,12 @@ __device__ __forceinline__ void chunk_update(WaveState &st, const float (&x)[U *
     }
   } else if (st.M != -kInf) {
     const float nR = -st.R;
-    const float S0 = st.S;
 #pragma unroll
     for (int e = 0; e < CH; ++e) {
-      const float d = fmaf(x[e], kLog2e, nR);
+      const float d = clamp_d(fmaf(x[e], kLog2e, nR));
       const float t = __builtin_amdgcn_exp2f(d);
       st.z += t;
       st.S = fmaf(t, d, st.S);
-    }
-    if (__builtin_amdgcn_ballot_w64(st.S != st.S) != 0) {
-      // a -inf logit made 0 * -inf: redo this chunk's S with clamped exponents
-      // (a NaN logit leaves z NaN and sends the row to the slow path anyway)
-      st.S = S0;
-#pragma unroll
-      for (int e = 0; e < CH; ++e) {
-        const float d = clamp_d(fmaf(x[e], kLog2e, nR));
-        st.S = fmaf(__builtin_amdgcn_exp2f(d), d, st.S);
-      }
     }
     if constexpr (ANY_ORDER) {
       if (__builtin_amdgcn_ballot_w64(cm == st.M) != 0)
@@ -364,13 +361,17 @@ __device__ void stream_slice(const StatsArgs &a, const T *row, int64_t lo, int64
     while (sp < a.n_suppress && a.suppress[sp] < base) ++sp;
     if (sp < a.n_suppress && a.suppress[sp] < base + STEP) {
       for (int q = sp; q < a.n_suppress && a.suppress[q] < base + STEP; ++q) {
-        const int64_t s = a.suppress[q];
+        // element (k, thread, e) of the iteration holds base + (k NT + thread) VEC + e;
+        // the owner and slot are uniform, so x stays in registers
+        const int off = (int)(a.suppress[q] - base);
+        const int ks = off / (NT * VEC), rs = off - ks * (NT * VEC);
+        const int owner = rs / VEC, es = rs - owner * VEC;
+        if (tid == owner) {
 #pragma unroll
-        for (int k = 0; k < U; ++k) {
-          const int64_t v0 = base + (int64_t)(k * NT + tid) * VEC;
+          for (int k = 0; k < U; ++k)
 #pragma unroll
-          for (int e = 0; e < VEC; ++e)
-            if (v0 + e == s) x[k * VEC + e] = -kInf;
+            for (int e = 0; e < VEC; ++e)
+              if (k == ks && e == es) x[k * VEC + e] = -kInf;
         }
       }
     }
@@ -420,7 +421,7 @@ __device__ void stream_slice(const StatsArgs &a, const T *row, int64_t lo, int64
       it = rot(it);
       const uint4 *q = p + it * ITER;
 #pragma unroll
-      for (int k = 0; k < U; ++k) r[k] = q[k * NT];
+      for (int k = 0; k < U; ++k) r[k] = load_stream(q + k * NT);
     };
     auto run = [&](const uint4 (&r)[U], int64_t it) {
       it = rot(it);
@@ -454,7 +455,7 @@ __device__ void stream_slice(const StatsArgs &a, const T *row, int64_t lo, int64
       for (int k = 0; k < U; ++k) {
         const int64_t v0 = tb + (int64_t)(k * NT + tid) * VEC;
         if (v0 < hi) {
-          const uint4 r = *reinterpret_cast<const uint4 *>(row + v0);
+          const uint4 r = load_stream(reinterpret_cast<const uint4 *>(row + v0));
 #pragma unroll
           for (int e = 0; e < VEC; ++e) x[k * VEC + e] = E::at(r, e);
         } else {
