@@ -29,6 +29,7 @@ from .stats import token_stats, token_stats_row, widen_logits, Stats
 from .rules import (threshold_transfer, topk_transfer, factor_transfer,
                     entropy_bound_transfer, edit_transfer, transfer_schedule,
                     block_ranges, block_causal_mask)
+from .step import commit_step, apply_step, counts, rank_rule, StepResult
 
 __all__ = [
     "philox4x32_10", "philox_words", "uniform_from_word", "gumbel_noise",
@@ -36,4 +37,5 @@ __all__ = [
     "threshold_transfer", "topk_transfer", "factor_transfer",
     "entropy_bound_transfer", "edit_transfer", "transfer_schedule",
     "block_ranges", "block_causal_mask",
+    "commit_step", "apply_step", "counts", "rank_rule", "StepResult",
 ]

@@ -15,6 +15,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
+PIN_FILES = ["test_oracle_pins.py", "test_oracle_step.py"]
+
 MUTATIONS = [
     # (file, original text, mutated text, -k selection of pin tests)
     ("stats.py", "((lp[keep] - m) - log_z)", "(lp[keep] - m)",
@@ -49,6 +51,13 @@ MUTATIONS = [
     ("rules.py", "start = (P // bl) * bl if align else P", "start = P", "block_ranges"),
     ("rules.py", "and _conf(prob[b, l]) > tau_edit", "and _conf(prob[b, l]) >= tau_edit",
      "edit"),
+    ("step.py", "take = (commit is not None and commit[b, l]) or (edit is not None and edit[b, l])",
+     "take = commit is not None and commit[b, l]", "hand_worked"),
+    ("step.py", "if cand[b, l] and not commit[b, l])", "if cand[b, l])", "hand_worked or block_loop"),
+    ("step.py", "c[b, 1] = sum(1 for l in range(edit.shape[1]) if edit[b, l])",
+     "c[b, 1] = 0", "hand_worked or editing_loop"),
+    ("step.py", "em = edit_transfer(st.x0, prob32, tokens, editable, tau_edit)",
+     "em = edit_transfer(st.x0, prob32, tokens, editable | cand, tau_edit)", "editing_loop"),
 ]
 
 
@@ -62,10 +71,11 @@ def test_planted_mistake_is_caught(case, tmp_path):
     assert old in src, f"mutation {case} no longer applies to {fname}"
     (dst / fname).write_text(src.replace(old, new, 1))
     shutil.copytree(os.path.join(ROOT, "tests", "golden"), tmp_path / "golden")
-    shutil.copy(os.path.join(ROOT, "tests", "test_oracle_pins.py"), tmp_path)
+    for pins in PIN_FILES:
+        shutil.copy(os.path.join(ROOT, "tests", pins), tmp_path)
     env = dict(os.environ, PYTHONPATH=str(tmp_path), PYTHONDONTWRITEBYTECODE="1")
     r = subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider",
-                        "-k", select, str(tmp_path / "test_oracle_pins.py")],
+                        "-k", select] + [str(tmp_path / pins) for pins in PIN_FILES],
                        cwd=tmp_path, env=env, capture_output=True, text=True, timeout=300)
     assert r.returncode == 1, (f"mutation {case} ({fname}) was not caught:\n"
                                + r.stdout[-2000:] + r.stderr[-2000:])
