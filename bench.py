@@ -42,6 +42,10 @@ def parse_args():
                    help="minimum host time spent timing the oracle")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain 1 GiB device copy (counter calibration)")
+    p.add_argument("--workload", default="diffusiongemma_canvas",
+                   choices=["diffusiongemma_canvas", "llada_block_loop"],
+                   help="diffusiongemma_canvas (default, the headline step) or llada_block_loop "
+                        "(the 32-step LLaDA block with dllm_commit_step, candidate rows only)")
     return p.parse_args()
 
 
@@ -106,6 +110,129 @@ def cpu_baseline(w, logit_bytes, min_seconds):
                       f"{reps} repetition(s), numpy float64 oracle in one process"}
 
 
+def llada_block_loop(args):
+    """The LLaDA block (B=1, L=32, V=126464 bf16, 32 steps, top-k with the even
+    quotas of transfer_schedule) as a loop of dllm_commit_step launches on the
+    device canvas, timed with HIP events; the candidate masks and quotas of
+    each step are recorded by one untimed pass first.  Run once reading only
+    the candidate rows and once reading every row; each is timed as eager
+    launches and as replays of the loop captured in a HIP graph."""
+    import numpy as np
+    import torch
+
+    import commit_step_amd as dc
+    import workloads
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    p = workloads.CONFIG_PARAMS[2]
+    B, L, V, steps, mask_id = p["B"], p["L"], p["V"], p["steps"], p["mask_id"]
+    logits = torch.empty((steps, B, L, V), dtype=torch.bfloat16, device=dev)
+    for s in range(steps):
+        w = workloads.config2_step(s)
+        logits[s].copy_(torch.from_numpy(w.logits.view(np.int16)).view(torch.bfloat16))
+    sup = w.suppress_ids
+    init = torch.full((B, L), mask_id, dtype=torch.int32, device=dev)
+    tok = init.clone()
+    counts_n = torch.full((B,), L, dtype=torch.int32, device=dev)
+    sched = dc.transfer_schedule(counts_n, steps)
+    x0 = torch.empty((B, L), dtype=torch.int32, device=dev)
+    pr = torch.empty((B, L), dtype=torch.float32, device=dev)
+    en = torch.empty((B, L), dtype=torch.float32, device=dev)
+    cands, ks, outs = [], [], []
+    for s in range(steps):                               # record the trajectory
+        cm = (tok == mask_id).to(torch.uint8)
+        k = sched[:, s].contiguous()
+        rule = dc.Rule.topk(cm, k)
+        dc.commit_step(logits[s], tok, [rule], suppress_ids=sup, out=(x0, pr, en))
+        cands.append(cm)
+        ks.append(k)
+        outs.append(rule.out)
+    torch.cuda.synchronize()
+    assert int((tok == mask_id).sum()) == 0, "the block did not finish"
+    read_rows = sum(int(c.sum()) for c in cands)
+    result = {}
+    lib = dc.load_library()
+    ws_bytes = int(lib.dllm_token_stats_workspace_size(dc.DLLM_BF16, B, L, V))
+    ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    supa = (ctypes.c_int32 * len(sup))(*sup)
+    fn = lib.dllm_commit_step
+    for skip in (True, False):
+        crules, canv, calls = [], [], []
+        for s in range(steps):                          # prebuilt C arguments
+            cr = (dc._CRule * 1)()
+            cr[0].kind, cr[0].mask, cr[0].out = dc.RULE_TOPK, cands[s].data_ptr(), outs[s].data_ptr()
+            cr[0].k = ks[s].data_ptr()
+            cv = dc._CCanvas()
+            cv.tokens, cv.counts, cv.skip_rows = tok.data_ptr(), None, int(skip)
+            crules.append(cr)
+            canv.append(cv)
+            calls.append((logits[s].data_ptr(), dc.DLLM_BF16, B, L, V, V, 0.0, 0, 0, supa, len(sup),
+                          x0.data_ptr(), pr.data_ptr(), en.data_ptr(), cr, 1, ctypes.byref(cv),
+                          ws.data_ptr(), ws.numel(), stream))
+
+        def loop():
+            tok.copy_(init)
+            rc = 0
+            for c in calls:
+                rc |= fn(*c)
+            if rc:
+                raise RuntimeError(lib.dllm_last_error().decode())
+        for _ in range(max(1, args.warmup // 10)):
+            loop()
+        torch.cuda.synchronize()
+        reps = max(1, args.steps // 10)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            loop()
+        b.record()
+        torch.cuda.synchronize()
+        ms_eager = a.elapsed_time(b) / reps
+        assert int((tok == mask_id).sum()) == 0
+        # the same loop captured once as a HIP graph (launch arguments are fixed
+        # at capture; no memset nodes) and replayed: device time without host gaps
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            cs = torch.cuda.current_stream(dev).cuda_stream
+            calls = [c[:-1] + (cs,) for c in calls]
+            loop()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            cs = torch.cuda.current_stream(dev).cuda_stream
+            calls = [c[:-1] + (cs,) for c in calls]
+            loop()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert int((tok == mask_id).sum()) == 0
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        ms_loop = a.elapsed_time(b) / reps
+        assert int((tok == mask_id).sum()) == 0
+        rows = read_rows if skip else steps * B * L
+        result[skip] = {"ms_per_loop": round(ms_loop, 4), "us_per_step": round(ms_loop * 1e3 / steps, 3),
+                        "us_per_step_eager": round(ms_eager * 1e3 / steps, 3),
+                        "logit_bytes_read": rows * V * 2,
+                        "logit_gb_s": round(rows * V * 2 / (ms_loop * 1e-3) / 1e9, 1)}
+    line = {"metric": "LLaDA block loop: commit steps/s (dllm_commit_step on the device canvas)",
+            "value": round(steps / (result[True]["ms_per_loop"] * 1e-3), 1), "unit": "steps/s",
+            "n_gpus": 1, "higher_is_better": True, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "llada_block_loop: B=1, L=32, V=126464 bf16, 32 steps, "
+                                   "topk with transfer_schedule quotas", "steps": steps},
+            "candidate_rows_only": result[True], "every_row": result[False],
+            "bytes_saved_frac": round(1 - read_rows / (steps * B * L), 4)}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -115,6 +242,9 @@ def main():
         sys.exit(2)
     if args.copy_probe:
         copy_probe()
+        return
+    if args.workload == "llada_block_loop":
+        llada_block_loop(args)
         return
 
     import numpy as np

@@ -19,7 +19,7 @@ import torch
 __all__ = ["Stats", "Rule", "token_stats", "threshold_transfer", "topk_transfer",
            "factor_transfer", "entropy_bound_transfer", "edit_transfer",
            "transfer_schedule", "block_ranges", "block_causal_mask",
-           "workspace_size", "library_path", "load_library"]
+           "workspace_size", "library_path", "load_library", "commit_step", "CommitStep"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libdllm_commit.so")
@@ -30,12 +30,18 @@ MAX_L = 4096
 MAX_SUPPRESS = 64
 
 Stats = namedtuple("Stats", ["x0", "prob", "entropy"])
+CommitStep = namedtuple("CommitStep", ["stats", "counts"])
 
 
 class _CRule(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int), ("mask", ctypes.c_void_p), ("out", ctypes.c_void_p),
                 ("param", ctypes.c_double), ("strict", ctypes.c_int),
                 ("k", ctypes.c_void_p), ("tokens", ctypes.c_void_p)]
+
+
+class _CCanvas(ctypes.Structure):
+    _fields_ = [("tokens", ctypes.c_void_p), ("counts", ctypes.c_void_p),
+                ("skip_rows", ctypes.c_int)]
 
 
 _lib = None
@@ -47,6 +53,9 @@ _SIGNATURES = {
                                 ctypes.c_uint64, _P, _I32, _P, _P, _P, _P, _I32, _P,
                                 ctypes.c_size_t, _P]),
     "dllm_token_stats_workspace_size": (ctypes.c_size_t, [_I32, _I64, _I64, _I64]),
+    "dllm_commit_step": (_I32, [_P, _I32, _I64, _I64, _I64, _I64, ctypes.c_float, ctypes.c_uint64,
+                                ctypes.c_uint64, _P, _I32, _P, _P, _P, _P, _I32, _P, _P,
+                                ctypes.c_size_t, _P]),
     "dllm_transfer_threshold": (_I32, [_P, _P, _I64, _I64, ctypes.c_double, _I32, _P, _P]),
     "dllm_transfer_topk": (_I32, [_P, _P, _P, _I64, _I64, _P, _P]),
     "dllm_transfer_factor": (_I32, [_P, _P, _I64, _I64, ctypes.c_double, _P, _P]),
@@ -157,6 +166,8 @@ class Rule:
 
     @classmethod
     def edit(cls, editable, tokens, tau_edit):
+        """tokens: the current canvas (may be None inside commit_step, which
+        passes its own canvas)."""
         return cls(RULE_EDIT, editable, tau_edit, tokens=tokens)
 
 
@@ -197,6 +208,44 @@ def token_stats(logits, temperature=0.0, seed=None, step=0, suppress_ids=(), rul
     of up to two Rule objects run in the same launch; their ``out`` tensors
     are filled.  ``out`` may give preallocated (x0, prob, entropy) tensors.
     """
+    return _stats_call(logits, temperature, seed, step, suppress_ids, rules, out, workspace,
+                       None)
+
+
+def commit_step(logits, tokens, rules, temperature=0.0, seed=None, step=0, suppress_ids=(),
+                skip_rows=True, counts=True, out=None, workspace=None):
+    """One step of the decoding loop in one launch: token_stats with up to one
+    ranking rule and one edit rule, then ``tokens`` (B, L) int32 is updated in
+    place to x0 wherever a position was committed or edited.
+
+    With ``skip_rows`` the logits of positions that no rule looks at are not
+    read (their x0 / prob / entropy are left as they were).  ``counts`` (True,
+    or a preallocated (B, 2) int32 tensor, device or pinned host) receives per
+    batch row the candidates left uncommitted and the positions edited.
+    Returns CommitStep(stats, counts).
+    """
+    B, L = logits.shape[0], logits.shape[1]
+    if tokens is not None:
+        _bl(tokens, "tokens", (torch.int32,), (B, L))
+    if counts is True:
+        counts = torch.empty((B, 2), dtype=torch.int32, device=logits.device)
+    elif counts is False:
+        counts = None
+    if counts is not None:
+        if counts.dtype != torch.int32 or tuple(counts.shape) != (B, 2) or not counts.is_contiguous():
+            raise ValueError("counts must be a contiguous (B, 2) int32 tensor")
+        if not (counts.is_cuda or counts.is_pinned()):
+            raise ValueError("counts must be device memory or pinned host memory")
+    canvas = _CCanvas()
+    canvas.tokens = tokens.data_ptr() if tokens is not None else None
+    canvas.counts = counts.data_ptr() if counts is not None else None
+    canvas.skip_rows = int(bool(skip_rows))
+    stats = _stats_call(logits, temperature, seed, step, suppress_ids, rules, out, workspace,
+                        (canvas, tokens, counts))
+    return CommitStep(stats, counts)
+
+
+def _stats_call(logits, temperature, seed, step, suppress_ids, rules, out, workspace, canvas):
     _dev(logits, "logits")
     if logits.dim() != 3:
         raise ValueError("logits must be (B, L, V)")
@@ -232,19 +281,26 @@ def token_stats(logits, temperature=0.0, seed=None, step=0, suppress_ids=(), rul
             keep.append(kt)
             c.k = kt.data_ptr()
         if r.kind == RULE_EDIT:
-            _bl(r.tokens, "tokens", (torch.int32,), (B, L))
-            c.tokens = r.tokens.data_ptr()
+            if r.tokens is None and canvas is None:
+                raise ValueError("the edit rule needs the current tokens")
+            if r.tokens is not None:
+                _bl(r.tokens, "tokens", (torch.int32,), (B, L))
+                c.tokens = r.tokens.data_ptr()
     dt = DLLM_BF16 if logits.dtype == torch.bfloat16 else DLLM_F32
     lib = load_library()
     with torch.cuda.device(dev):
         need = int(lib.dllm_token_stats_workspace_size(dt, B, L, V))
         ws = workspace if workspace is not None else _workspace(dev, need)
-        _check(lib.dllm_token_stats(
-            logits.data_ptr(), dt, B, L, V, row_stride, float(temperature),
-            int(seed or 0) & 0xFFFFFFFFFFFFFFFF, int(step), sup, len(suppress_ids),
-            x0.data_ptr(), prob.data_ptr(), ent.data_ptr(),
-            crules if len(rules) else None, len(rules), ws.data_ptr(), ws.numel(),
-            _stream(logits)), "dllm_token_stats")
+        args = [logits.data_ptr(), dt, B, L, V, row_stride, float(temperature),
+                int(seed or 0) & 0xFFFFFFFFFFFFFFFF, int(step), sup, len(suppress_ids),
+                x0.data_ptr(), prob.data_ptr(), ent.data_ptr(),
+                crules if len(rules) else None, len(rules)]
+        if canvas is None:
+            _check(lib.dllm_token_stats(*args, ws.data_ptr(), ws.numel(), _stream(logits)),
+                   "dllm_token_stats")
+        else:
+            _check(lib.dllm_commit_step(*args, ctypes.byref(canvas[0]), ws.data_ptr(),
+                                        ws.numel(), _stream(logits)), "dllm_commit_step")
     return Stats(x0, prob, ent)
 
 

@@ -44,6 +44,7 @@ namespace dllm {
 constexpr float kInf = __builtin_inff();
 constexpr int kIdxNone = 0x7fffffff;
 constexpr int kMaxRules = 2;
+constexpr int kMaxSlices = 256;   // slices of one row (partials merged in LDS)
 
 struct Partial {          // one row slice's statistics (workspace)
   float M;                // max of the slice (-inf: empty)
@@ -112,9 +113,15 @@ struct StatsArgs {
   uint8_t *edit_out;
   const int32_t *edit_tokens;
   double edit_tau;
+  // canvas step (dllm_commit_step)
+  int skip_rows;           // rows in no rule's mask are neither read nor written
+  int need_batch;          // run the batch-row completion (rank rules or counts)
+  int32_t *canvas;         // (B, L) tokens, updated in place, or NULL
+  int32_t *counts;         // (B, 2) candidates left uncommitted, positions edited; or NULL
   // workspace
   uint32_t *batch_count;   // [B]
   uint32_t *row_count;     // [B*L] (slices > 1)
+  uint32_t *edit_count;    // [B] edits of the batch row (counts only)
   Partial *partials;       // [B*L*slices] (slices > 1)
 };
 
@@ -612,9 +619,114 @@ __device__ RowResult slow_row(const StatsArgs &a, const T *row, uint32_t b, uint
   return r;
 }
 
+// Does any fused rule look at this row?
+__device__ __forceinline__ bool row_needed(const StatsArgs &a, int64_t row_id) {
+  bool need = a.has_edit && a.edit_mask[row_id];
+  for (int r = 0; r < a.n_rank_rules; ++r) need = need || a.rank_rules[r].mask[row_id];
+  return need;
+}
+
+// Statistics of a finished row from its merged partial; false when the row is
+// degenerate (NaN, +inf, or no finite unsuppressed logit) and needs the
+// two-pass path.
+template <bool SAMPLE>
+__device__ __forceinline__ bool finalize_partial(const Partial &p, RowResult &res) {
+  const bool ok = bits_finite(__float_as_uint(p.M)) && bits_finite(__float_as_uint(p.z)) &&
+                  bits_finite(__float_as_uint(p.S)) &&
+                  (!SAMPLE || (p.ib != kIdxNone && bits_finite(__float_as_uint(p.sb))));
+  if (ok) {
+    const float zf = 1.0f + p.z;
+    res.ent = log1pf(p.z) - kLn2 * p.S / zf;
+    if (SAMPLE) {
+      res.x0 = p.ib;
+      res.prob = __builtin_amdgcn_exp2f((p.xb - p.M) * kLog2e) / zf;
+    } else {
+      res.x0 = p.idx;
+      res.prob = 1.0f / zf;
+    }
+  }
+  return ok;
+}
+
+// Writes one row's statistics (coherent: the batch-row finisher and the
+// rules read them) and decides its edit; returns 1 if the row was edited.
+__device__ __forceinline__ int publish_row(const StatsArgs &a, int64_t row_id,
+                                           const RowResult &res) {
+  store_coherent(&a.x0[row_id], res.x0);
+  store_coherent(&a.prob[row_id], res.prob);
+  store_coherent(&a.entropy[row_id], res.ent);
+  if (!a.has_edit) return 0;
+  const uint8_t e = edit_decision(a.edit_mask[row_id], res.x0, a.edit_tokens[row_id],
+                                  res.prob, a.edit_tau);
+  a.edit_out[row_id] = e;
+  if (e && a.canvas) a.canvas[row_id] = res.x0;      // this row's own token
+  return e;
+}
+
+// Canvas update for the committed positions of batch row b and its counts.
+// Runs in the workgroup that completed the batch row, after the rank rule
+// (whose output this workgroup has just written).  edits < 0: the edit count
+// is in the workspace.
+__device__ inline void finish_canvas(const StatsArgs &a, uint32_t b, int edits) {
+  __shared__ int s_left[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  const int64_t L = a.L, base = (int64_t)b * L;
+  int left = 0;
+  if (a.n_rank_rules) {
+    const RuleDev &r = a.rank_rules[0];
+    for (int64_t l = tid; l < L; l += blockDim.x) {
+      const bool committed = r.out[base + l] != 0;
+      if (committed && a.canvas) a.canvas[base + l] = load_coh(&a.x0[base + l]);
+      left += (r.mask[base + l] && !committed) ? 1 : 0;
+    }
+  }
+  if (a.counts) {
+    const int w = wave_sum_i(left);
+    if (lane == 0) s_left[wave] = w;
+    __syncthreads();
+    if (tid == 0) {
+      int tot = 0;
+      for (int i = 0; i < nw; ++i) tot += s_left[i];
+      if (edits < 0) {
+        edits = (int)load_coh(&a.edit_count[b]);
+        a.edit_count[b] = 0u;        // leave the workspace zeroed
+      }
+      a.counts[2 * b] = tot;
+      a.counts[2 * b + 1] = edits;
+    }
+  }
+}
+
+// The batch row's statistics are all published: rank rules, canvas, counts.
+__device__ inline void complete_batch_row(const StatsArgs &a, uint32_t b, unsigned char *smem,
+                                          int edits) {
+  for (int r = 0; r < a.n_rank_rules; ++r)
+    run_batch_rule(a.rank_rules[r], (int)b, (int)a.L, a.prob, a.entropy, smem);
+  if (a.canvas || a.counts) finish_canvas(a, b, edits);
+  if (threadIdx.x == 0) a.batch_count[b] = 0u;   // leave the workspace zeroed
+}
+
+// Whole rows: after a row's statistics are published, count the row into its
+// batch row; the workgroup that completes the batch row runs the rank rules on
+// the statistics the launch has just written (coherent loads), then the canvas
+// update and the counts.
+__device__ inline void finish_row(const StatsArgs &a, uint32_t b, unsigned char *smem) {
+  __shared__ int s_last;
+  const int tid = threadIdx.x;
+  if (!a.need_batch) return;
+  if (tid == 0) {
+    wait_stores_complete();
+    const uint32_t prev = atomicAdd(&a.batch_count[b], 1u);
+    s_last = (prev == (uint32_t)(a.L - 1));
+  }
+  __syncthreads();
+  if (!s_last) return;
+  complete_batch_row(a, b, smem, -1);
+}
+
 template <typename T, int NT, int UV, bool SAMPLE, bool VECLOAD>
 __global__ __launch_bounds__(NT) void token_stats_kernel(StatsArgs a) {
-  extern __shared__ __align__(16) unsigned char smem[];   // rules (dynamic)
+  extern __shared__ __align__(16) unsigned char smem[];   // slice partials, then the rules
   __shared__ Partial wave_parts[NT / 64];
   __shared__ Partial slice_parts_acc;
   __shared__ int s_flag;
@@ -629,87 +741,61 @@ __global__ __launch_bounds__(NT) void token_stats_kernel(StatsArgs a) {
   const int64_t lo = (int64_t)slice * a.slice_len;
   const int64_t hi = min(lo + a.slice_len, a.V);
 
+  // Candidate-row skipping: a row that no rule looks at is not read, and its
+  // statistics are left as they were; an edit rule's output for it is 0.
+  // Slice 0 still counts it into its batch row.
+  if (a.skip_rows && !row_needed(a, row_id)) {
+    if (slice != 0) return;
+    if (tid == 0 && a.has_edit) a.edit_out[row_id] = 0;
+    finish_row(a, b, smem);
+    return;
+  }
+
   stream_slice<T, NT, UV, SAMPLE, VECLOAD>(a, row, lo, hi, b, l, wave_parts, &slice_parts_acc);
 
-  // Split rows: publish the slice partial; the last slice to finish merges.
+  // Split rows: publish the slice partial and count it on the row's own
+  // counter (a counter per row keeps the atomics of a launch spread out); the
+  // last slice to arrive fetches every slice's partial at once into LDS and
+  // merges them in slice order.
   if (a.slices > 1) {
+    Partial *parts = &a.partials[row_id * a.slices];
     if (tid == 0) {
-      // publish the slice partial, count the slice; the last slice merges
-      store_partial(&a.partials[row_id * a.slices + slice], slice_parts_acc);
+      store_partial(&parts[slice], slice_parts_acc);
       wait_stores_complete();
       const uint32_t prev = atomicAdd(&a.row_count[row_id], 1u);
       s_flag = (prev == (uint32_t)(a.slices - 1));
-      if (s_flag) {
-        Partial *parts = &a.partials[row_id * a.slices];
-        Partial acc = load_partial(&parts[0]);
-        for (int s = 1; s < a.slices; ++s) {
-          const Partial q = load_partial(&parts[s]);
-          merge_partial(acc, q);
-          if (SAMPLE) merge_sample(acc, q);
-        }
-        slice_parts_acc = acc;
-        // Leave the workspace zero-filled: the counter and the partials (a
-        // later call of another shape may lay its counters over them).
-        for (int s = 0; s < a.slices; ++s) {
-          uint4 *w = reinterpret_cast<uint4 *>(&parts[s]);
-          w[0] = make_uint4(0u, 0u, 0u, 0u);
-          w[1] = make_uint4(0u, 0u, 0u, 0u);
-        }
-        a.row_count[row_id] = 0u;
-      }
     }
     __syncthreads();
     if (!s_flag) return;
+    Partial *lds = reinterpret_cast<Partial *>(smem);    // [slices], before the rules use it
+    for (int s = tid; s < a.slices; s += NT) {
+      lds[s] = load_partial(&parts[s]);
+      uint4 *w = reinterpret_cast<uint4 *>(&parts[s]);   // leave the record zero-filled
+      w[0] = make_uint4(0u, 0u, 0u, 0u);
+      w[1] = make_uint4(0u, 0u, 0u, 0u);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      Partial acc = lds[0];
+      for (int s = 1; s < a.slices; ++s) {       // fixed slice order: reproducible
+        merge_partial(acc, lds[s]);
+        if (SAMPLE) merge_sample(acc, lds[s]);
+      }
+      slice_parts_acc = acc;
+      a.row_count[row_id] = 0u;
+    }
+    __syncthreads();
   }
 
   // Finalize the row.
   __shared__ int s_slow;
   RowResult res;
   res.x0 = 0; res.prob = 0.f; res.ent = 0.f;
-  if (tid == 0) {
-    const Partial p = slice_parts_acc;
-    const bool ok = bits_finite(__float_as_uint(p.M)) && bits_finite(__float_as_uint(p.z)) &&
-                    bits_finite(__float_as_uint(p.S)) &&
-                    (!SAMPLE || (p.ib != kIdxNone && bits_finite(__float_as_uint(p.sb))));
-    s_slow = !ok;
-    if (ok) {
-      const float zf = 1.0f + p.z;
-      res.ent = log1pf(p.z) - kLn2 * p.S / zf;
-      if (SAMPLE) {
-        res.x0 = p.ib;
-        res.prob = __builtin_amdgcn_exp2f((p.xb - p.M) * kLog2e) / zf;
-      } else {
-        res.x0 = p.idx;
-        res.prob = 1.0f / zf;
-      }
-    }
-  }
+  if (tid == 0) s_slow = !finalize_partial<SAMPLE>(slice_parts_acc, res);
   __syncthreads();
   if (s_slow) res = slow_row<T, NT, SAMPLE>(a, row, b, l, slow_scratch);
-
-  if (tid == 0) {
-    a.x0[row_id] = res.x0;
-    store_coherent(&a.prob[row_id], res.prob);       // read by the batch-row rules
-    store_coherent(&a.entropy[row_id], res.ent);
-    if (a.has_edit)
-      a.edit_out[row_id] = edit_decision(a.edit_mask[row_id], res.x0, a.edit_tokens[row_id],
-                                         res.prob, a.edit_tau);
-  }
-  if (a.n_rank_rules == 0) return;
-
-  // Batch-row rules: the workgroup that completes the batch row runs them.
-  // Thread 0 counts its row in once its statistics are published; the rules
-  // read the others' with coherent loads.
-  if (tid == 0) {
-    wait_stores_complete();
-    const uint32_t prev = atomicAdd(&a.batch_count[b], 1u);
-    s_flag = (prev == (uint32_t)(a.L - 1));
-  }
-  __syncthreads();
-  if (!s_flag) return;
-  for (int r = 0; r < a.n_rank_rules; ++r)
-    run_batch_rule(a.rank_rules[r], (int)b, (int)a.L, a.prob, a.entropy, smem);
-  if (tid == 0) a.batch_count[b] = 0u;   // leave the workspace zeroed
+  if (tid == 0 && publish_row(a, row_id, res) && a.counts) atomicAdd(&a.edit_count[b], 1u);
+  finish_row(a, b, smem);
 }
 
 // ---------------------------------------------------------------- host side
@@ -741,6 +827,7 @@ Plan make_plan(int dtype, int64_t rows, int64_t V, int64_t row_stride, const voi
     int64_t s = (cus + rows - 1) / rows;
     const int64_t min_slice = 4096;               // keep slices worth a launch
     s = std::min<int64_t>(s, std::max<int64_t>(1, V / min_slice));
+    s = std::min<int64_t>(s, kMaxSlices);
     p.slices = (int)std::max<int64_t>(1, s);
   }
   int64_t sl = (V + p.slices - 1) / p.slices;
@@ -750,8 +837,10 @@ Plan make_plan(int dtype, int64_t rows, int64_t V, int64_t row_stride, const voi
   return p;
 }
 
+// Workspace: batch-row counters [B], edit counts [B], then for split rows the
+// row counters [B*L] and the partials [B*L*slices], each region 256-byte aligned.
 size_t workspace_bytes_for(int64_t B, int64_t L, int slices) {
-  size_t bytes = ((size_t)B * 4 + 255) / 256 * 256;
+  size_t bytes = 2 * (((size_t)B * 4 + 255) / 256 * 256);
   if (slices > 1) {
     bytes += ((size_t)B * L * 4 + 255) / 256 * 256;
     bytes += (size_t)B * L * slices * sizeof(Partial);
@@ -798,30 +887,33 @@ extern "C" size_t dllm_token_stats_workspace_size(int dtype, int64_t B, int64_t 
   return workspace_bytes_for(B, L, p.slices);
 }
 
-extern "C" int dllm_token_stats(const void *logits, int dtype, int64_t B, int64_t L, int64_t V,
-                                int64_t row_stride, float temperature, uint64_t seed,
-                                uint64_t step, const int32_t *suppress_ids, int n_suppress,
-                                int32_t *x0, float *prob, float *entropy,
-                                const dllm_rule *rules, int n_rules, void *workspace,
-                                size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+// Both entry points: validation, workspace layout and the launch.  `canvas`
+// is NULL for dllm_token_stats.
+int stats_step(const char *who, const void *logits, int dtype, int64_t B, int64_t L, int64_t V,
+               int64_t row_stride, float temperature, uint64_t seed, uint64_t step,
+               const int32_t *suppress_ids, int n_suppress, int32_t *x0, float *prob,
+               float *entropy, const dllm_rule *rules, int n_rules, const dllm_canvas *canvas,
+               void *workspace, size_t workspace_bytes, hipStream_t stream) {
   if (dtype != DLLM_F32 && dtype != DLLM_BF16)
-    return fail(DLLM_ERR_DTYPE, "dllm_token_stats: dtype %d is neither DLLM_F32 nor DLLM_BF16", dtype);
-  if (B < 0 || L < 0) return fail(DLLM_ERR_ARG, "dllm_token_stats: B and L must be >= 0");
+    return fail(DLLM_ERR_DTYPE, "%s: dtype %d is neither DLLM_F32 nor DLLM_BF16", who, dtype);
+  if (B < 0 || L < 0) return fail(DLLM_ERR_ARG, "%s: B and L must be >= 0", who);
   if (V < 1 || V > 0x7fffffffLL)
-    return fail(DLLM_ERR_ARG, "dllm_token_stats: V = %lld must be in [1, 2^31)", (long long)V);
-  if (row_stride < V) return fail(DLLM_ERR_ARG, "dllm_token_stats: row_stride < V");
+    return fail(DLLM_ERR_ARG, "%s: V = %lld must be in [1, 2^31)", who, (long long)V);
+  if (row_stride < V) return fail(DLLM_ERR_ARG, "%s: row_stride < V", who);
   if (!(temperature >= 0.0f) || temperature == __builtin_inff())
-    return fail(DLLM_ERR_ARG, "dllm_token_stats: temperature must be finite and >= 0");
-  if (step > 0xffffffffull) return fail(DLLM_ERR_ARG, "dllm_token_stats: step must be < 2^32");
+    return fail(DLLM_ERR_ARG, "%s: temperature must be finite and >= 0", who);
+  if (step > 0xffffffffull) return fail(DLLM_ERR_ARG, "%s: step must be < 2^32", who);
   if (n_suppress < 0 || n_suppress > DLLM_MAX_SUPPRESS)
-    return fail(DLLM_ERR_ARG, "dllm_token_stats: n_suppress must be in [0, %d]", DLLM_MAX_SUPPRESS);
+    return fail(DLLM_ERR_ARG, "%s: n_suppress must be in [0, %d]", who, DLLM_MAX_SUPPRESS);
   if (n_suppress > 0 && !suppress_ids)
-    return fail(DLLM_ERR_ARG, "dllm_token_stats: suppress_ids is NULL");
+    return fail(DLLM_ERR_ARG, "%s: suppress_ids is NULL", who);
   if (n_rules < 0 || n_rules > kMaxRules || (n_rules > 0 && !rules))
-    return fail(DLLM_ERR_ARG, "dllm_token_stats: n_rules must be 0..%d with a rules array", kMaxRules);
+    return fail(DLLM_ERR_ARG, "%s: n_rules must be 0..%d with a rules array", who, kMaxRules);
   if (B == 0 || L == 0) return ok();
   if (!logits || !x0 || !prob || !entropy)
-    return fail(DLLM_ERR_ARG, "dllm_token_stats: logits, x0, prob and entropy must be non-NULL");
+    return fail(DLLM_ERR_ARG, "%s: logits, x0, prob and entropy must be non-NULL", who);
 
   StatsArgs a;
   memset(&a, 0, sizeof(a));
@@ -829,15 +921,15 @@ extern "C" int dllm_token_stats(const void *logits, int dtype, int64_t B, int64_
   for (int i = 0; i < n_suppress; ++i) {
     const int32_t s = suppress_ids[i];
     if (s < 0 || s >= V)
-      return fail(DLLM_ERR_ARG, "dllm_token_stats: suppress id %d is outside [0, V)", s);
+      return fail(DLLM_ERR_ARG, "%s: suppress id %d is outside [0, V)", who, s);
     int j = i;
     while (j > 0 && a.suppress[j - 1] > s) { a.suppress[j] = a.suppress[j - 1]; --j; }
     a.suppress[j] = s;
   }
   for (int i = 1; i < n_suppress; ++i)
     if (a.suppress[i] == a.suppress[i - 1])
-      return fail(DLLM_ERR_ARG, "dllm_token_stats: suppress id %d appears twice", a.suppress[i]);
-  if (n_suppress >= V) return fail(DLLM_ERR_ARG, "dllm_token_stats: every id is suppressed");
+      return fail(DLLM_ERR_ARG, "%s: suppress id %d appears twice", who, a.suppress[i]);
+  if (n_suppress >= V) return fail(DLLM_ERR_ARG, "%s: every id is suppressed", who);
   int first_allowed = 0;
   for (int i = 0; i < n_suppress && a.suppress[i] == first_allowed; ++i) ++first_allowed;
 
@@ -847,47 +939,66 @@ extern "C" int dllm_token_stats(const void *logits, int dtype, int64_t B, int64_
   for (int i = 0; i < n_rules; ++i) {
     const dllm_rule &r = rules[i];
     if (r.kind < DLLM_RULE_THRESHOLD || r.kind > DLLM_RULE_EDIT)
-      return fail(DLLM_ERR_ARG, "dllm_token_stats: rules[%d].kind = %d is not a DLLM_RULE_*", i, r.kind);
-    if (seen[r.kind]) return fail(DLLM_ERR_ARG, "dllm_token_stats: rule kind %d appears twice", r.kind);
+      return fail(DLLM_ERR_ARG, "%s: rules[%d].kind = %d is not a DLLM_RULE_*", who, i, r.kind);
+    if (seen[r.kind]) return fail(DLLM_ERR_ARG, "%s: rule kind %d appears twice", who, r.kind);
     seen[r.kind] = true;
     outs[i] = r.out;
     if (r.out == (const void *)x0 || r.out == (const void *)prob || r.out == (const void *)entropy ||
         r.out == (const void *)r.mask || r.out == (const void *)logits)
-      return fail(DLLM_ERR_ARG, "dllm_token_stats: rules[%d].out aliases another array", i);
+      return fail(DLLM_ERR_ARG, "%s: rules[%d].out aliases another array", who, i);
     if (r.kind == DLLM_RULE_EDIT) {
-      if (!r.mask || !r.out || !r.tokens)
-        return fail(DLLM_ERR_ARG, "dllm_token_stats: edit rule needs mask, out and tokens");
-      if (r.param != r.param) return fail(DLLM_ERR_ARG, "dllm_token_stats: tau_edit is NaN");
+      const bool canvas_tokens = canvas && canvas->tokens;
+      if (!r.mask || !r.out || (!r.tokens && !canvas_tokens))
+        return fail(DLLM_ERR_ARG, "%s: edit rule needs mask, out and tokens", who);
+      if (canvas_tokens && r.tokens && r.tokens != canvas->tokens)
+        return fail(DLLM_ERR_ARG, "%s: the edit rule's tokens must be the canvas", who);
+      if (r.param != r.param) return fail(DLLM_ERR_ARG, "%s: tau_edit is NaN", who);
       a.has_edit = 1;
       a.edit_mask = r.mask;
       a.edit_out = r.out;
-      a.edit_tokens = r.tokens;
+      a.edit_tokens = r.tokens ? r.tokens : canvas->tokens;
       a.edit_tau = r.param;
     } else {
       if (L > DLLM_MAX_L)
-        return fail(DLLM_ERR_UNSUPPORTED, "dllm_token_stats: L = %lld exceeds DLLM_MAX_L = %d",
+        return fail(DLLM_ERR_UNSUPPORTED, "%s: L = %lld exceeds DLLM_MAX_L = %d", who,
                     (long long)L, DLLM_MAX_L);
-      const int rc = prepare_rule(r, a.rank_rules[a.n_rank_rules], B, L, "dllm_token_stats");
+      const int rc = prepare_rule(r, a.rank_rules[a.n_rank_rules], B, L, who);
       if (rc != DLLM_OK) return rc;
       ++a.n_rank_rules;
     }
   }
   if (n_rules == 2 && outs[0] == outs[1])
-    return fail(DLLM_ERR_ARG, "dllm_token_stats: the two rules share an output");
+    return fail(DLLM_ERR_ARG, "%s: the two rules share an output", who);
+  if (canvas) {
+    if (a.n_rank_rules > 1)
+      return fail(DLLM_ERR_ARG, "%s: a canvas step takes at most one ranking rule", who);
+    const void *arrays[] = {logits, x0, prob, entropy, outs[0], outs[1]};
+    for (const void *q : arrays)
+      if (q && (q == (const void *)canvas->tokens || q == (const void *)canvas->counts))
+        return fail(DLLM_ERR_ARG, "%s: canvas tokens or counts alias another array", who);
+    if (canvas->tokens && (const void *)canvas->tokens == (const void *)canvas->counts)
+      return fail(DLLM_ERR_ARG, "%s: canvas tokens and counts alias", who);
+    a.canvas = canvas->tokens;
+    a.counts = canvas->counts;
+    a.skip_rows = canvas->skip_rows ? 1 : 0;
+  }
+  a.need_batch = (a.n_rank_rules > 0 || a.counts) ? 1 : 0;
 
   const int64_t rows = B * L;
   const Plan p = make_plan(dtype, rows, V, row_stride, logits);
   const size_t need = workspace_bytes_for(B, L, p.slices);
-  if (!workspace) return fail(DLLM_ERR_ARG, "dllm_token_stats: workspace is NULL");
+  if (!workspace) return fail(DLLM_ERR_ARG, "%s: workspace is NULL", who);
   if (workspace_bytes < need)
-    return fail(DLLM_ERR_SHAPE, "dllm_token_stats: workspace has %zu bytes, this shape needs %zu",
+    return fail(DLLM_ERR_SHAPE, "%s: workspace has %zu bytes, this shape needs %zu", who,
                 workspace_bytes, need);
   if ((uintptr_t)workspace % 16)
-    return fail(DLLM_ERR_ARG, "dllm_token_stats: workspace must be 16-byte aligned");
+    return fail(DLLM_ERR_ARG, "%s: workspace must be 16-byte aligned", who);
 
   unsigned char *ws = static_cast<unsigned char *>(workspace);
   a.batch_count = reinterpret_cast<uint32_t *>(ws);
   size_t off = ((size_t)B * 4 + 255) / 256 * 256;
+  a.edit_count = reinterpret_cast<uint32_t *>(ws + off);
+  off += ((size_t)B * 4 + 255) / 256 * 256;
   if (p.slices > 1) {
     a.row_count = reinterpret_cast<uint32_t *>(ws + off);
     off += ((size_t)rows * 4 + 255) / 256 * 256;
@@ -910,11 +1021,37 @@ extern "C" int dllm_token_stats(const void *logits, int dtype, int64_t B, int64_
   a.entropy = entropy;
 
   const bool sample = temperature > 0.0f;
-  const size_t smem = a.n_rank_rules ? rule_smem_bytes((int)L, p.nt) : 0;
+  size_t smem = a.n_rank_rules ? rule_smem_bytes((int)L, p.nt) : 0;
+  if (p.slices > 1) smem = std::max(smem, (size_t)p.slices * sizeof(Partial));
   hipError_t e;
   if (dtype == DLLM_BF16) e = launch_plan<uint16_t>(p, a, rows, sample, smem, stream);
   else e = launch_plan<float>(p, a, rows, sample, smem, stream);
   if (e != hipSuccess)
-    return fail(DLLM_ERR_HIP, "dllm_token_stats: launch failed: %s", hipGetErrorString(e));
+    return fail(DLLM_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" int dllm_token_stats(const void *logits, int dtype, int64_t B, int64_t L, int64_t V,
+                                int64_t row_stride, float temperature, uint64_t seed,
+                                uint64_t step, const int32_t *suppress_ids, int n_suppress,
+                                int32_t *x0, float *prob, float *entropy,
+                                const dllm_rule *rules, int n_rules, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+  return stats_step("dllm_token_stats", logits, dtype, B, L, V, row_stride, temperature, seed,
+                    step, suppress_ids, n_suppress, x0, prob, entropy, rules, n_rules, nullptr,
+                    workspace, workspace_bytes, stream);
+}
+
+extern "C" int dllm_commit_step(const void *logits, int dtype, int64_t B, int64_t L, int64_t V,
+                                int64_t row_stride, float temperature, uint64_t seed,
+                                uint64_t step, const int32_t *suppress_ids, int n_suppress,
+                                int32_t *x0, float *prob, float *entropy,
+                                const dllm_rule *rules, int n_rules, const dllm_canvas *canvas,
+                                void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!canvas) return fail(DLLM_ERR_ARG, "dllm_commit_step: canvas is NULL");
+  return stats_step("dllm_commit_step", logits, dtype, B, L, V, row_stride, temperature, seed,
+                    step, suppress_ids, n_suppress, x0, prob, entropy, rules, n_rules, canvas,
+                    workspace, workspace_bytes, stream);
 }

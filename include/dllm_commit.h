@@ -141,6 +141,53 @@ int dllm_token_stats(const void *logits, int dtype, int64_t B, int64_t L,
 size_t dllm_token_stats_workspace_size(int dtype, int64_t B, int64_t L,
                                        int64_t V);
 
+/* ---------------------------------------------------------------------------
+ * dllm_commit_step: one step of the decoding loops, in one launch.
+ *
+ * The loops of mlx-arsenal "dLLM block decoding" (the block loop of section
+ * "The pattern" and the loop of section "Token editing (LLaDA2.1)") do, per
+ * step: statistics, a commit rule over the masked candidates, an edit rule
+ * over the committed positions of the block, then x <- where(commit | edit,
+ * x0, x), and test on the host whether a mask is left and whether anything
+ * was edited.  mojo-dllm ("Why the runtime looks different", few rows need
+ * logits) computes logits only for the candidate rows.  This call does all of
+ * it on the device:
+ *   - exactly dllm_token_stats with the same rules (at most one ranking rule
+ *     and at most one edit rule), on the same workspace;
+ *   - with skip_rows != 0, a position that is in no rule's mask is not read:
+ *     its x0, prob and entropy are left as they were (its logits may be
+ *     anything), and its edit output is 0;
+ *   - with tokens != NULL, tokens[b, l] = x0[b, l] wherever the ranking rule
+ *     committed or the edit rule edited; other tokens are left as they were;
+ *   - with counts != NULL, counts[2b] = candidates of the ranking rule left
+ *     uncommitted in batch row b (0 without one) and counts[2b + 1] =
+ *     positions edited in batch row b.  counts may be device memory or
+ *     host-pinned memory mapped into the device's address space (then
+ *     readable on the host once the stream has passed this call).
+ *
+ *   tokens  (B, L) int32 DEVICE, read and written (the edit rule's current
+ *           tokens: an edit rule's own tokens pointer must be NULL or this).
+ *   counts  (B, 2) int32, written.
+ * tokens and counts must not alias any other array of the call.
+ * Errors: as dllm_token_stats, plus DLLM_ERR_ARG for a NULL canvas, two
+ * ranking rules, or aliasing.
+ * -------------------------------------------------------------------------*/
+typedef struct {
+  int32_t *tokens;   /* (B, L) canvas updated in place, or NULL */
+  int32_t *counts;   /* (B, 2) left / edited per batch row, or NULL */
+  int skip_rows;     /* nonzero: rows in no rule's mask are not read */
+} dllm_canvas;
+
+int dllm_commit_step(const void *logits, int dtype, int64_t B, int64_t L,
+                     int64_t V, int64_t row_stride, float temperature,
+                     uint64_t seed, uint64_t step,
+                     const int32_t *suppress_ids, int n_suppress,
+                     int32_t *x0, float *prob, float *entropy,
+                     const dllm_rule *rules, int n_rules,
+                     const dllm_canvas *canvas,
+                     void *workspace, size_t workspace_bytes,
+                     hipStream_t stream);
+
 /* threshold_transfer ("What mlx-arsenal ships", threshold_transfer row; mlxcel
  * "Block Diffusion", "LLaDA-2 Block Unmasking"): per batch row, commit every
  * candidate with conf >= tau (conf > tau when strict != 0); if no candidate

@@ -103,6 +103,35 @@ def test_token_stats_argument_errors(lib):
     assert call(B=0) == 0 and call(L=0) == 0
 
 
+def test_commit_step_argument_errors(lib):
+    import commit_step_amd as dc
+    P = ctypes.c_void_p
+    fake = P(16)   # never dereferenced: every call below fails validation first
+
+    def call(canvas, rules=None, nrules=0, B=1, L=4, V=8):
+        return lib.dllm_commit_step(fake, 1, B, L, V, V, 0.0, 0, 0, None, 0, fake, P(24), P(40),
+                                    rules, nrules, canvas, fake, 1 << 20, None)
+
+    assert call(None) == -1 and "canvas" in _err(lib)
+    cv = dc._CCanvas()
+    cv.tokens, cv.counts, cv.skip_rows = 64, 64, 1
+    assert call(ctypes.byref(cv)) == -1 and "alias" in _err(lib)
+    cv.counts = 24                                    # the prob array
+    assert call(ctypes.byref(cv)) == -1 and "alias" in _err(lib)
+    cv.counts = 80
+    rules = (dc._CRule * 2)()
+    for i, kind in enumerate((dc.RULE_THRESHOLD, dc.RULE_TOPK)):
+        rules[i].kind, rules[i].mask, rules[i].out, rules[i].param = kind, 96 + i, 128 + i, 0.5
+        rules[i].k = 160
+    assert call(ctypes.byref(cv), rules, 2) == -1 and "ranking rule" in _err(lib)
+    rules[1].kind, rules[1].tokens = dc.RULE_EDIT, 200   # an edit rule with other tokens
+    assert call(ctypes.byref(cv), rules, 2) == -1 and "canvas" in _err(lib)
+    cv.tokens = None
+    rules[1].tokens = None                            # no tokens anywhere
+    assert call(ctypes.byref(cv), rules, 2) == -1 and "tokens" in _err(lib)
+    assert call(ctypes.byref(cv), B=0) == 0
+
+
 def test_transfer_argument_errors(lib):
     fake = ctypes.c_void_p(16)
     assert lib.dllm_transfer_threshold(fake, fake, 1, 4, math.nan, 0, ctypes.c_void_p(32), None) == -1
