@@ -18,6 +18,11 @@ Readings of the pages taken here (each also listed in the design doc):
     first maximal one);
   * sampled x0 is the first index of the maximum of logit / T + g, with g the
     Gumbel noise of oracle.philox (Gumbel-max trick);
+  * margin is the topk_margin confidence of mojo-dllm "The GPU path" (row
+    statistics paragraph: p minus the runner-up's probability, the runner-up
+    being the largest logit at any index other than the argmax): p_(1) - p_(2)
+    of softmax(logits) over the unsuppressed ids, whatever x0 is; a tie at the
+    maximum gives 0, a single unsuppressed id gives 1;
   * "NaN-safe": a NaN logit counts as -inf; a row whose unsuppressed logits are
     all -inf (or NaN) is uniform over the unsuppressed ids; a row with +inf
     logits is uniform over its +inf ids.  These are the limits of finite rows,
@@ -35,7 +40,7 @@ import numpy as np
 
 from .philox import gumbel_noise
 
-Stats = namedtuple("Stats", ["x0", "prob", "entropy"])
+Stats = namedtuple("Stats", ["x0", "prob", "entropy", "margin"])
 
 
 def widen_logits(logits, dtype):
@@ -69,7 +74,7 @@ def token_stats_row(ell, temperature, seed, step, b, l, suppressed):
 
     ell: float64 (V,) logits; temperature: the float32 value as float;
     suppressed: bool (V,) mask of suppressed ids (not all True).
-    Returns (x0, prob, entropy) as (int, float, float).
+    Returns (x0, prob, entropy, margin) as (int, float, float, float).
     """
     V = ell.shape[0]
     allowed = ~suppressed
@@ -94,13 +99,19 @@ def token_stats_row(ell, temperature, seed, step, b, l, suppressed):
         p = w / z
         keep = allowed & (p > 0.0)
         H = -np.sum(p[keep] * ((lp[keep] - m) - log_z))
+        # runner-up: the largest logit at any allowed index but the top one
+        r = -np.inf
+        for v in np.flatnonzero(allowed):
+            if v != top and lp[v] > r:
+                r = lp[v]
+        margin = -np.expm1(r - m) / z                    # (1 - e^(r - m)) / z
         if sampling:
             with np.errstate(invalid="ignore"):
                 s = lp / temperature + g
             x0 = _first_argmax(s, allowed)
         else:
             x0 = _first_argmax(lp, allowed)
-        return x0, float(p[x0]), float(H)
+        return x0, float(p[x0]), float(H), float(margin)
 
     # Degenerate rows: the limit of finite rows.
     if m == -np.inf:
@@ -109,18 +120,18 @@ def token_stats_row(ell, temperature, seed, step, b, l, suppressed):
         support = allowed & (ell == np.inf)     # uniform over the +inf ids
     n = int(support.sum())
     x0 = _first_argmax(g, support) if sampling else int(np.flatnonzero(support)[0])
-    return x0, 1.0 / n, float(np.log(n))
+    return x0, 1.0 / n, float(np.log(n)), (1.0 if n == 1 else 0.0)
 
 
 def token_stats(logits, dtype="f32", temperature=0.0, seed=None, step=0,
                 suppress_ids=(), positions=None):
-    """Per-position (x0, prob, entropy) of (B, L, V) logits.
+    """Per-position (x0, prob, entropy, margin) of (B, L, V) logits.
 
     temperature: 0 = greedy; > 0 = Gumbel-max with key ``seed`` at ``step``
     (``seed`` is required then, as the pages require an explicit key).  The
     temperature is taken as the float32 value a C caller would pass.
     positions: optional iterable of (b, l); then only those are computed and the
-    other outputs are left at x0 = -1, prob = entropy = NaN.
+    other outputs are left at x0 = -1, prob = entropy = margin = NaN.
     """
     a = np.asarray(logits)
     if a.ndim != 3:
@@ -139,9 +150,10 @@ def token_stats(logits, dtype="f32", temperature=0.0, seed=None, step=0,
     x0 = np.full((B, L), -1, dtype=np.int32)
     prob = np.full((B, L), np.nan)
     ent = np.full((B, L), np.nan)
+    mar = np.full((B, L), np.nan)
     todo = positions if positions is not None else ((b, l) for b in range(B) for l in range(L))
     for b, l in todo:
         row = widen_logits(a[b, l], dtype)
-        x0[b, l], prob[b, l], ent[b, l] = token_stats_row(
+        x0[b, l], prob[b, l], ent[b, l], mar[b, l] = token_stats_row(
             row, T, seed if seed is not None else 0, step, b, l, suppressed)
-    return Stats(x0, prob, ent)
+    return Stats(x0, prob, ent, mar)

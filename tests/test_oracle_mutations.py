@@ -51,6 +51,9 @@ MUTATIONS = [
     ("rules.py", "start = (P // bl) * bl if align else P", "start = P", "block_ranges"),
     ("rules.py", "and _conf(prob[b, l]) > tau_edit", "and _conf(prob[b, l]) >= tau_edit",
      "edit"),
+    ("stats.py", "if v != top and lp[v] > r:", "if lp[v] > r:", "margin"),
+    ("stats.py", "margin = -np.expm1(r - m) / z", "margin = (1.0 - np.exp(r - m)) / z", "margin"),
+    ("stats.py", "(1.0 if n == 1 else 0.0)", "0.0", "margin"),
     ("step.py", "take = (commit is not None and commit[b, l]) or (edit is not None and edit[b, l])",
      "take = commit is not None and commit[b, l]", "hand_worked"),
     ("step.py", "if cand[b, l] and not commit[b, l])", "if cand[b, l])", "hand_worked or block_loop"),

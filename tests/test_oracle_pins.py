@@ -24,12 +24,20 @@ def _golden_rows(name):
         return [ln.split() for ln in fh if ln.strip() and not ln.startswith("#")]
 
 
-def _stats1(row, T=0.0, seed=0, step=0, b=0, l=0, suppress=()):
+def _stats4(row, T=0.0, seed=0, step=0, b=0, l=0, suppress=()):
+    row = np.asarray(row, dtype=np.float64)
     V = row.shape[0]
     sup = np.zeros(V, dtype=bool)
     sup[list(suppress)] = True
-    return oracle.token_stats_row(np.asarray(row, dtype=np.float64), float(np.float32(T)),
-                                  seed, step, b, l, sup)
+    return oracle.token_stats_row(row, float(np.float32(T)), seed, step, b, l, sup)
+
+
+def _stats1(row, **kw):
+    return _stats4(row, **kw)[:3]
+
+
+def _margin(row, **kw):
+    return _stats4(row, **kw)[3]
 
 
 # ----------------------------------------------------------------- token stats
@@ -48,6 +56,77 @@ def test_one_hot_row():
     row[1234] = 1000.0
     x0, p, H = _stats1(row)
     assert (x0, p, H) == (1234, 1.0, 0.0)
+
+
+# ----------------------------------------------------------------- margin
+# mojo-dllm "The GPU path", row statistics paragraph: topk_margin is p minus the
+# runner-up's probability, the runner-up being the largest logit at any other
+# index.
+
+@pytest.mark.parametrize("V,k,a,bv", [(10, 1, 2.0, -1.0), (100, 1, 0.5, 0.0), (4096, 1, 9.0, -3.0),
+                                      (50, 2, 3.0, 0.0), (777, 5, 1.0, -1.0)])
+def test_margin_two_level_closed_form(V, k, a, bv):
+    rng = np.random.default_rng(V * 3 + k)
+    row = np.full(V, bv)
+    row[rng.choice(V, size=k, replace=False)] = a
+    want = (math.exp(a) - math.exp(bv)) / (math.exp(a) + (V - 1) * math.exp(bv)) if k == 1 else 0.0
+    assert _margin(row) == pytest.approx(want, rel=1e-13, abs=0)
+
+
+def test_margin_three_level_closed_form():
+    V, h1, h2 = 300, 7.0, 5.5
+    row = np.zeros(V)
+    row[42], row[17] = h1, h2
+    want = (math.exp(h1) - math.exp(h2)) / (math.exp(h1) + math.exp(h2) + V - 2)
+    assert _margin(row) == pytest.approx(want, rel=1e-13)
+
+
+@pytest.mark.parametrize("delta", [1e-3, 1e-7, 1e-10])
+def test_margin_near_tie_is_tanh(delta):
+    # two ids, logits 0 and -delta: p1 - p2 = tanh(delta / 2), relatively exact
+    # even where 1 - e^-delta would cancel
+    assert _margin([0.0, -delta]) == pytest.approx(math.tanh(delta / 2), rel=1e-12, abs=0)
+
+
+def test_margin_limits_and_degenerate_rows():
+    assert _margin(np.full(9, 1.5)) == 0.0                          # uniform
+    row = np.zeros(20); row[[3, 11]] = 4.0
+    assert _margin(row) == 0.0                                      # tie at the maximum
+    assert _margin(np.arange(6.0), suppress=(0, 1, 2, 3, 4)) == 1.0  # one id left
+    row = np.zeros(8); row[5] = np.inf
+    assert _margin(row) == 1.0                                      # one +inf id
+    row[2] = np.inf
+    assert _margin(row) == 0.0                                      # two +inf ids
+    assert _margin(np.full(5, -np.inf)) == 0.0                      # uniform over 5
+    assert _margin(np.full(5, np.nan), suppress=(0, 1, 2, 3)) == 1.0
+
+
+def test_margin_brute_force_tiny_rows():
+    rng = np.random.default_rng(17)
+    for _ in range(300):
+        V = int(rng.integers(1, 12))
+        row = rng.standard_normal(V) * 3
+        row[rng.random(V) < 0.15] = np.nan
+        sup = tuple(v for v in range(V) if rng.random() < 0.2)
+        if len(sup) == V:
+            sup = sup[1:]
+        allowed = [v for v in range(V) if v not in sup]
+        vals = np.array([-np.inf if np.isnan(row[v]) else row[v] for v in allowed])
+        if np.isneginf(vals).all():
+            p = np.full(len(allowed), 1.0 / len(allowed))
+        else:
+            e = np.exp(vals - vals.max())
+            p = e / e.sum()
+        p = np.sort(p)[::-1]
+        want = p[0] - (p[1] if len(p) > 1 else 0.0)
+        assert _margin(row, suppress=sup) == pytest.approx(want, rel=1e-11, abs=1e-15)
+
+
+def test_margin_does_not_depend_on_sampling():
+    row = np.random.default_rng(3).standard_normal(500) * 2
+    g = _margin(row)
+    for T, seed in ((0.7, 5), (2.0, 99)):
+        assert _margin(row, T=T, seed=seed) == g
 
 
 @pytest.mark.parametrize("V,k,a,bv", [(10, 1, 2.0, -1.0), (100, 3, 0.5, 0.0), (4096, 7, 9.0, -3.0)])
@@ -206,7 +285,7 @@ def test_gumbel_max_frequencies_follow_tempered_softmax(T):
     sup = np.zeros(V, dtype=bool)
     Tf = float(np.float32(T))
     for i in range(n):
-        x0, _, _ = oracle.token_stats_row(ell, Tf, 2024, 0, i % 97, i // 97, sup)
+        x0, _, _, _ = oracle.token_stats_row(ell, Tf, 2024, 0, i % 97, i // 97, sup)
         counts[x0] += 1
     p = np.exp(ell / Tf - (ell / Tf).max())
     p /= p.sum()
