@@ -169,7 +169,7 @@ def llada_block_loop(args):
             crules.append(cr)
             canv.append(cv)
             calls.append((logits[s].data_ptr(), dc.DLLM_BF16, B, L, V, V, 0.0, 0, 0, supa, len(sup),
-                          x0.data_ptr(), pr.data_ptr(), en.data_ptr(), cr, 1, ctypes.byref(cv),
+                          x0.data_ptr(), pr.data_ptr(), en.data_ptr(), None, cr, 1, ctypes.byref(cv),
                           ws.data_ptr(), ws.numel(), stream))
 
         def loop():
@@ -283,7 +283,7 @@ def main():
     rules[1].param, rules[1].tokens = p["tau_edit"], tokens.data_ptr()
     stream = torch.cuda.current_stream(dev).cuda_stream
     call_args = [(rot[i].data_ptr(), dc.DLLM_BF16, B, L, V, V, 0.0, 0, 0, None, 0,
-                  x0.data_ptr(), prob.data_ptr(), ent.data_ptr(), rules, 2, ws.data_ptr(),
+                  x0.data_ptr(), prob.data_ptr(), ent.data_ptr(), None, rules, 2, ws.data_ptr(),
                   ws.numel(), stream) for i in range(R)]
     fn = lib.dllm_token_stats
 

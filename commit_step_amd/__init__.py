@@ -26,17 +26,19 @@ _LIB_PATH = os.path.join(_HERE, "libdllm_commit.so")
 
 DLLM_F32, DLLM_BF16 = 0, 1
 RULE_THRESHOLD, RULE_TOPK, RULE_FACTOR, RULE_ENTROPY_BOUND, RULE_EDIT = 1, 2, 3, 4, 5
+SCORE_PROB, SCORE_MARGIN, SCORE_NEG_ENTROPY = 0, 1, 2
+_SCORES = {"prob": SCORE_PROB, "margin": SCORE_MARGIN, "neg_entropy": SCORE_NEG_ENTROPY}
 MAX_L = 4096
 MAX_SUPPRESS = 64
 
-Stats = namedtuple("Stats", ["x0", "prob", "entropy"])
+Stats = namedtuple("Stats", ["x0", "prob", "entropy", "margin"])
 CommitStep = namedtuple("CommitStep", ["stats", "counts"])
 
 
 class _CRule(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int), ("mask", ctypes.c_void_p), ("out", ctypes.c_void_p),
                 ("param", ctypes.c_double), ("strict", ctypes.c_int),
-                ("k", ctypes.c_void_p), ("tokens", ctypes.c_void_p)]
+                ("k", ctypes.c_void_p), ("tokens", ctypes.c_void_p), ("score", ctypes.c_int)]
 
 
 class _CCanvas(ctypes.Structure):
@@ -50,11 +52,11 @@ _lib = None
 _I64, _I32, _P = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
 _SIGNATURES = {
     "dllm_token_stats": (_I32, [_P, _I32, _I64, _I64, _I64, _I64, ctypes.c_float, ctypes.c_uint64,
-                                ctypes.c_uint64, _P, _I32, _P, _P, _P, _P, _I32, _P,
+                                ctypes.c_uint64, _P, _I32, _P, _P, _P, _P, _P, _I32, _P,
                                 ctypes.c_size_t, _P]),
     "dllm_token_stats_workspace_size": (ctypes.c_size_t, [_I32, _I64, _I64, _I64]),
     "dllm_commit_step": (_I32, [_P, _I32, _I64, _I64, _I64, _I64, ctypes.c_float, ctypes.c_uint64,
-                                ctypes.c_uint64, _P, _I32, _P, _P, _P, _P, _I32, _P, _P,
+                                ctypes.c_uint64, _P, _I32, _P, _P, _P, _P, _P, _I32, _P, _P,
                                 ctypes.c_size_t, _P]),
     "dllm_transfer_threshold": (_I32, [_P, _P, _I64, _I64, ctypes.c_double, _I32, _P, _P]),
     "dllm_transfer_topk": (_I32, [_P, _P, _P, _I64, _I64, _P, _P]),
@@ -144,21 +146,26 @@ class Rule:
     result lands in ``rule.out`` (a bool (B, L) tensor).
     """
 
-    def __init__(self, kind, mask, param=0.0, strict=False, k=None, tokens=None, out=None):
+    def __init__(self, kind, mask, param=0.0, strict=False, k=None, tokens=None, out=None,
+                 score="prob"):
+        if score not in _SCORES:
+            raise ValueError(f"score must be one of {sorted(_SCORES)}")
         self.kind, self.mask, self.param, self.strict = kind, mask, float(param), bool(strict)
-        self.k, self.tokens, self.out = k, tokens, out
+        self.k, self.tokens, self.out, self.score = k, tokens, out, _SCORES[score]
 
     @classmethod
-    def threshold(cls, candidates, tau, strict=False):
-        return cls(RULE_THRESHOLD, candidates, tau, strict=strict)
+    def threshold(cls, candidates, tau, strict=False, score="prob"):
+        """score: "prob" (LLaDA, maskgit_plus), "margin" (topk_margin) or
+        "neg_entropy" (Dream's entropy confidence)."""
+        return cls(RULE_THRESHOLD, candidates, tau, strict=strict, score=score)
 
     @classmethod
-    def topk(cls, candidates, k):
-        return cls(RULE_TOPK, candidates, k=k)
+    def topk(cls, candidates, k, score="prob"):
+        return cls(RULE_TOPK, candidates, k=k, score=score)
 
     @classmethod
-    def factor(cls, candidates, f):
-        return cls(RULE_FACTOR, candidates, f)
+    def factor(cls, candidates, f, score="prob"):
+        return cls(RULE_FACTOR, candidates, f, score=score)
 
     @classmethod
     def entropy_bound(cls, candidates, gamma):
@@ -200,20 +207,22 @@ def _row_stride(logits):
 
 
 def token_stats(logits, temperature=0.0, seed=None, step=0, suppress_ids=(), rules=(),
-                out=None, workspace=None):
-    """Per-position (x0, prob, entropy) of (B, L, V) float32 / bfloat16 logits.
+                out=None, workspace=None, margin=False):
+    """Per-position (x0, prob, entropy, margin) of (B, L, V) float32 / bfloat16 logits.
 
     temperature > 0 draws x0 by Gumbel-max and then needs an explicit ``seed``
     (an integer key; ``step`` selects the per-step noise).  ``rules`` is a list
     of up to two Rule objects run in the same launch; their ``out`` tensors
-    are filled.  ``out`` may give preallocated (x0, prob, entropy) tensors.
+    are filled.  ``margin`` (or a rule ranking by margin) adds the topk_margin
+    confidence p1 - p2; otherwise Stats.margin is None.  ``out`` may give
+    preallocated (x0, prob, entropy[, margin]) tensors.
     """
     return _stats_call(logits, temperature, seed, step, suppress_ids, rules, out, workspace,
-                       None)
+                       None, margin)
 
 
 def commit_step(logits, tokens, rules, temperature=0.0, seed=None, step=0, suppress_ids=(),
-                skip_rows=True, counts=True, out=None, workspace=None):
+                skip_rows=True, counts=True, out=None, workspace=None, margin=False):
     """One step of the decoding loop in one launch: token_stats with up to one
     ranking rule and one edit rule, then ``tokens`` (B, L) int32 is updated in
     place to x0 wherever a position was committed or edited.
@@ -241,11 +250,12 @@ def commit_step(logits, tokens, rules, temperature=0.0, seed=None, step=0, suppr
     canvas.counts = counts.data_ptr() if counts is not None else None
     canvas.skip_rows = int(bool(skip_rows))
     stats = _stats_call(logits, temperature, seed, step, suppress_ids, rules, out, workspace,
-                        (canvas, tokens, counts))
+                        (canvas, tokens, counts), margin)
     return CommitStep(stats, counts)
 
 
-def _stats_call(logits, temperature, seed, step, suppress_ids, rules, out, workspace, canvas):
+def _stats_call(logits, temperature, seed, step, suppress_ids, rules, out, workspace, canvas,
+                margin):
     _dev(logits, "logits")
     if logits.dim() != 3:
         raise ValueError("logits must be (B, L, V)")
@@ -256,15 +266,22 @@ def _stats_call(logits, temperature, seed, step, suppress_ids, rules, out, works
     if temperature > 0 and seed is None:
         raise ValueError("sampling (temperature > 0) needs an explicit seed")
     dev = logits.device
+    want_margin = bool(margin) or any(getattr(r, "score", 0) == SCORE_MARGIN for r in rules)
+    mar = None
     if out is None:
         x0 = torch.empty((B, L), dtype=torch.int32, device=dev)
         prob = torch.empty((B, L), dtype=torch.float32, device=dev)
         ent = torch.empty((B, L), dtype=torch.float32, device=dev)
     else:
-        x0, prob, ent = out
+        x0, prob, ent = out[0], out[1], out[2]
+        mar = out[3] if len(out) > 3 else None
         _bl(x0, "x0", (torch.int32,), (B, L))
         _bl(prob, "prob", (torch.float32,), (B, L))
         _bl(ent, "entropy", (torch.float32,), (B, L))
+    if want_margin and mar is None:
+        mar = torch.empty((B, L), dtype=torch.float32, device=dev)
+    if mar is not None:
+        _bl(mar, "margin", (torch.float32,), (B, L))
     sup = (ctypes.c_int32 * max(len(suppress_ids), 1))(*[int(s) for s in suppress_ids])
     crules = (_CRule * 2)()
     keep = []
@@ -275,7 +292,7 @@ def _stats_call(logits, temperature, seed, step, suppress_ids, rules, out, works
         _bl(r.out, "rule out", _MASK_DTYPES, (B, L))
         c = crules[i]
         c.kind, c.mask, c.out = r.kind, r.mask.data_ptr(), r.out.data_ptr()
-        c.param, c.strict = r.param, int(r.strict)
+        c.param, c.strict, c.score = r.param, int(r.strict), r.score
         if r.kind == RULE_TOPK:
             kt = _k_tensor(r.k, B, dev)
             keep.append(kt)
@@ -294,6 +311,7 @@ def _stats_call(logits, temperature, seed, step, suppress_ids, rules, out, works
         args = [logits.data_ptr(), dt, B, L, V, row_stride, float(temperature),
                 int(seed or 0) & 0xFFFFFFFFFFFFFFFF, int(step), sup, len(suppress_ids),
                 x0.data_ptr(), prob.data_ptr(), ent.data_ptr(),
+                mar.data_ptr() if mar is not None else None,
                 crules if len(rules) else None, len(rules)]
         if canvas is None:
             _check(lib.dllm_token_stats(*args, ws.data_ptr(), ws.numel(), _stream(logits)),
@@ -301,7 +319,7 @@ def _stats_call(logits, temperature, seed, step, suppress_ids, rules, out, works
         else:
             _check(lib.dllm_commit_step(*args, ctypes.byref(canvas[0]), ws.data_ptr(),
                                         ws.numel(), _stream(logits)), "dllm_commit_step")
-    return Stats(x0, prob, ent)
+    return Stats(x0, prob, ent, mar)
 
 
 def _rule_out(conf, candidates, out):

@@ -8,7 +8,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SOURCES = ["csrc/token_stats.hip", "csrc/transfer.hip"]
+SOURCES = ["csrc/token_stats.hip", "csrc/token_stats_full.hip", "csrc/transfer.hip"]
 LIB = os.path.join(HERE, "libdllm_commit.so")
 
 FLAGS = [
@@ -28,21 +28,44 @@ def hipcc():
     return "hipcc"
 
 
+def _filter(out):
+    return [ln for ln in out.strip().splitlines() if "argument unused during compilation" not in ln
+            and "packed-fp32-ops" not in ln]
+
+
 def build(verbose=True):
-    """Compile the HIP sources into commit_step_amd/libdllm_commit.so."""
+    """Compile the HIP sources into commit_step_amd/libdllm_commit.so: one
+    object per source, compiled in parallel, then one link."""
+    inc = ["-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc")]
+    cflags = [f for f in FLAGS if f != "-shared"]
+    objs, procs = [], []
+    for src in SOURCES:
+        obj = os.path.join(HERE, os.path.basename(src) + ".o")
+        cmd = [hipcc(), *cflags, *inc, "-c", "-o", obj, os.path.join(HERE, src)]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        objs.append(obj)
+        procs.append(subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                                      text=True))
+    failed = []
+    for src, pr in zip(SOURCES, procs):
+        out, _ = pr.communicate()
+        lines = _filter(out)
+        if pr.returncode != 0:
+            failed.append(f"{src}:\n" + "\n".join(lines))
+        elif verbose and lines:
+            print("\n".join(lines), flush=True)
+    if failed:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(failed))
     tmp = LIB + ".tmp"
-    cmd = [hipcc(), *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc"),
-           "-o", tmp, *[os.path.join(HERE, s) for s in SOURCES]]
+    cmd = [hipcc(), "--offload-arch=gfx950", "-fPIC", "-shared", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
-    out = (r.stdout + r.stderr).strip()
-    lines = [ln for ln in out.splitlines() if "argument unused during compilation" not in ln
-             and "packed-fp32-ops" not in ln]
     if r.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(lines))
-    if verbose and lines:
-        print("\n".join(lines), flush=True)
+        raise RuntimeError("link failed:\n" + "\n".join(_filter(r.stdout + r.stderr)))
+    for obj in objs:
+        os.remove(obj)
     os.replace(tmp, LIB)
     return LIB
 

@@ -31,6 +31,8 @@ constexpr uint64_t kSentinel = ~0ull;
 struct RuleDev {
   int kind;
   int strict;
+  int score;           // fused ranking rules: which statistic is the confidence
+  int negate;          // confidence = -score array (Dream's negative entropy)
   const uint8_t *mask;
   uint8_t *out;
   const int32_t *k;
@@ -82,6 +84,13 @@ __device__ inline RuleSmem rule_smem(unsigned char *base, int L) {
 
 __device__ __forceinline__ float load_coherent(const float *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// A ranking rule's confidence from its score array (negated for a negative
+// entropy; NaN stays NaN and counts as -inf).
+__device__ __forceinline__ float rule_conf(const RuleDev &r, const float *p) {
+  const float v = load_coherent(p);
+  return r.negate ? -v : v;
 }
 
 // (i + 1) * (1 - c) <= f, exactly: (i+1)*c is exact in float64 (a 24-bit
@@ -235,7 +244,7 @@ __device__ inline void short_rank_rule(const RuleDev &r, int b, int L, const flo
   const uint8_t *m_row = r.mask + (int64_t)b * L;
   uint8_t *o_row = r.out + (int64_t)b * L;
   const bool cand = t < L && m_row[t];
-  const float c = cand ? conf_sanitized(load_coherent(conf + (int64_t)b * L + t)) : 0.f;
+  const float c = cand ? conf_sanitized(rule_conf(r, conf + (int64_t)b * L + t)) : 0.f;
   const uint64_t key = cand ? (((uint64_t)conf_key(c) << 32) | (uint32_t)t) : kSentinel;
   int *wcnt = sm.misc, *wfail = sm.misc + 32;
   const uint64_t m = __builtin_amdgcn_ballot_w64(cand);
@@ -393,7 +402,7 @@ __device__ inline int sort_candidates(const RuleDev &r, int b, int L, const floa
   for (int i = tid; i < Np; i += nt) {
     uint64_t key = kSentinel;
     if (i < L && m_row[i]) {
-      const float v = load_coherent(s_row + i);
+      const float v = by_entropy ? load_coherent(s_row + i) : rule_conf(r, s_row + i);
       const uint32_t hk = by_entropy ? ent_key(v) : conf_key(v);
       key = ((uint64_t)hk << 32) | (uint32_t)i;
       ++mine;
@@ -483,7 +492,7 @@ __device__ inline void rule_threshold(const RuleDev &r, int b, int L, const floa
   for (int l = tid; l < L; l += nt) {
     uint8_t v = 0;
     if (m_row[l]) {
-      const float c = conf_sanitized(load_coherent(c_row + l));
+      const float c = conf_sanitized(rule_conf(r, c_row + l));
       const double cd = (double)c;
       v = (r.strict ? (cd > r.param) : (cd >= r.param)) ? 1 : 0;
       my_pass += v;

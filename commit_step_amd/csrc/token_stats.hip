@@ -1,813 +1,18 @@
-// dllm_token_stats: one pass over (B, L, V) logits -> (x0, prob, entropy) per
-// position, optionally followed, in the same launch, by the commit rules.
-//
-// What is computed: mlx-arsenal research note "dLLM block decoding", "What
-// mlx-arsenal ships", token_stats row (proposed token, its probability and the
-// entropy, float32, NaN-safe, greedy or Gumbel-max with an explicit key,
-// suppress_ids removed before the softmax); mojo-dllm "The GPU path", row
-// statistics paragraph (first index of the maximum; p = 1/z; the entropy from
-// sum e^(x-m) and sum e^(x-m)(x-m)).
-//
-// Design for gfx950.  The step reads B*L*V logits once and does a few dozen
-// operations per element, so it is bound by HBM bandwidth, with the vector ALU
-// close behind for bf16; there is no dense contraction and no MFMA.
-//   * Each workgroup streams one row (or a slice of one) with 16-byte loads;
-//     consecutive lanes read consecutive 16 bytes, so every wave load is 1 KiB
-//     contiguous.  The next chunk is loaded while the current one is reduced.
-//   * One pass, where the page's device kernel makes two: the running maximum M
-//     is shared by the 64 lanes of a wave (a DPP max per chunk), so a rise of M
-//     is a rare, wave-uniform event.  Each lane accumulates, relative to M and
-//     in base 2, z- = sum of 2^d over every element except one maximal element,
-//     and S = sum 2^d d, d = (x - M) log2 e.  Keeping the maximal element out of
-//     z- keeps log z = log1p(z-) accurate for peaked rows (z close to 1); it is
-//     excluded exactly once, in the chunk where M rises.
-//   * Wave partials (M, first index of M, z-, S) merge associatively through
-//     LDS; a row split over several workgroups merges its slices through the
-//     caller's workspace, in slice order, so results are bit-reproducible.
-//   * prob = 1 / (1 + z-) (greedy) and H = log1p(z-) - ln2 * S / (1 + z-).
-//   * Rows holding NaN or +inf, or whose unsuppressed logits are all -inf, are
-//     detected after the pass and recomputed by a plain two-pass loop with the
-//     exact limit semantics.
-//   * Fused rules: the workgroup that finishes the last position of a batch row
-//     (a counter in the workspace) runs the ranking rules on the statistics the
-//     launch has just written; the edit rule is decided per position.
+// dllm_token_stats and dllm_commit_step: host side (validation, workspace,
+// launch plan) and the plain statistics kernels.  The kernels themselves are
+// in token_stats_dev.h.
 #include <stdarg.h>
 #include <string.h>
 
 #include <algorithm>
 
-#include "common.h"
-#include "rules_dev.h"
+#include "token_stats_dev.h"
 
 namespace dllm {
-
-constexpr float kInf = __builtin_inff();
-constexpr int kIdxNone = 0x7fffffff;
-constexpr int kMaxRules = 2;
-constexpr int kMaxSlices = 256;   // slices of one row (partials merged in LDS)
-
-struct Partial {          // one row slice's statistics (workspace)
-  float M;                // max of the slice (-inf: empty)
-  int idx;                // first index of M
-  float z;                // sum 2^((x-M)log2e) over the slice but one maximal element
-  float S;                // sum 2^d d, d = (x-M)log2e
-  float sb;               // sampled: best score x/T + g
-  int ib;                 // sampled: its index
-  float xb;               // sampled: its logit
-  int pad;
-};
-static_assert(sizeof(Partial) == 32, "Partial is zeroed as two 16-byte words");
-
-// Publishing to other workgroups of the same launch, which may run on other
-// XCDs (each with its own L2): values are written with agent-scope atomic
-// stores (coherent at device level), the writer waits until they have
-// completed, and only then counts itself in with a device-scope atomic; the
-// reader, having seen the count, reads them with agent-scope atomic loads.
-// This is the mechanism an agent-scope release/acquire uses for atomic data,
-// without the writeback of the whole L2 that non-atomic data would need.
-template <typename V>
-__device__ __forceinline__ void store_coherent(V *p, V v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-template <typename V>
-__device__ __forceinline__ V load_coh(const V *p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void wait_stores_complete() { __builtin_amdgcn_s_waitcnt(0); }
-
-__device__ __forceinline__ void store_partial(Partial *dst, const Partial &p) {
-  store_coherent(&dst->M, p.M); store_coherent(&dst->idx, p.idx);
-  store_coherent(&dst->z, p.z); store_coherent(&dst->S, p.S);
-  store_coherent(&dst->sb, p.sb); store_coherent(&dst->ib, p.ib);
-  store_coherent(&dst->xb, p.xb);
-}
-__device__ __forceinline__ Partial load_partial(const Partial *src) {
-  Partial p;
-  p.M = load_coh(&src->M); p.idx = load_coh(&src->idx);
-  p.z = load_coh(&src->z); p.S = load_coh(&src->S);
-  p.sb = load_coh(&src->sb); p.ib = load_coh(&src->ib);
-  p.xb = load_coh(&src->xb); p.pad = 0;
-  return p;
-}
-
-struct StatsArgs {
-  const void *logits;
-  int64_t row_stride;
-  int64_t V;
-  int64_t L;
-  int64_t slice_len;       // elements per slice (multiple of 8)
-  int slices;
-  float inv_temp;
-  uint32_t key0, key1, step;
-  int n_suppress;
-  int first_allowed;       // lowest id not suppressed
-  int32_t suppress[DLLM_MAX_SUPPRESS];   // sorted ascending
-  int32_t *x0;
-  float *prob;
-  float *entropy;
-  // fused rules
-  int n_rank_rules;
-  RuleDev rank_rules[kMaxRules];
-  int has_edit;
-  const uint8_t *edit_mask;
-  uint8_t *edit_out;
-  const int32_t *edit_tokens;
-  double edit_tau;
-  // canvas step (dllm_commit_step)
-  int skip_rows;           // rows in no rule's mask are neither read nor written
-  int need_batch;          // run the batch-row completion (rank rules or counts)
-  int32_t *canvas;         // (B, L) tokens, updated in place, or NULL
-  int32_t *counts;         // (B, 2) candidates left uncommitted, positions edited; or NULL
-  // workspace
-  uint32_t *batch_count;   // [B]
-  uint32_t *row_count;     // [B*L] (slices > 1)
-  uint32_t *edit_count;    // [B] edits of the batch row (counts only)
-  Partial *partials;       // [B*L*slices] (slices > 1)
-};
-
-// Logits are read exactly once: 16-byte loads with the non-temporal hint, so
-// the stream does not churn L2 and the Infinity Cache.
-__device__ __forceinline__ uint4 load_stream(const uint4 *p) {
-  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-template <typename T> struct ElemT;
-template <> struct ElemT<uint16_t> {   // bf16 bit patterns
-  static constexpr int VEC = 8;        // elements per 16-byte load
-  static constexpr int U = 4;          // loads per lane per chunk
-  __device__ static float at(const uint4 &v, int e) {
-    const uint32_t w = e < 2 ? v.x : e < 4 ? v.y : e < 6 ? v.z : v.w;
-    return (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
-  }
-  __device__ static float load1(const uint16_t *p) { return __uint_as_float((uint32_t)*p << 16); }
-};
-template <> struct ElemT<float> {
-  static constexpr int VEC = 4;
-  static constexpr int U = 8;
-  __device__ static float at(const uint4 &v, int e) {
-    const uint32_t w = e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
-    return __uint_as_float(w);
-  }
-  __device__ static float load1(const float *p) { return *p; }
-};
-
-// Wave-local running state.  Weights are taken against the reference
-// R = RN(M log2 e): an element x weighs 2^(x log2e - R), its exponent one fma,
-// so x log2 e is never rounded on its own.  The wave partial is converted to
-// weights relative to M itself (2^((x - M) log2 e)) when the stream ends,
-// using the exact residual M log2e - R.
-struct WaveState {
-  float M;       // wave-uniform running max
-  float R;       // wave-uniform reference RN(M log2 e)
-  int idx;       // wave-uniform first index of M
-  float zx, Sx;  // wave-uniform: demoted maxima and ties of M, against R
-  float z, S;    // per lane, against R
-  float sb;      // per lane sampled best
-  int ib;
-  float xb;
-};
-
-__device__ __forceinline__ float clamp_d(float d) {
-  // d <= a tiny positive residual; below -200 (and -inf) the term 2^d is 0 in
-  // float32.  An unsigned min on the bits maps every such d (and -inf) to -200
-  // while leaving [-200, +inf) untouched, so 0 * -inf never arises.  NaN d
-  // passes through.
-  return __uint_as_float(min(__float_as_uint(d), 0xC3480000u));
-}
-
-// Process one chunk: every lane holds CH = U * VEC elements, element j of load
-// k at index idx_of(k, j, lane).  A chunk that raises the wave maximum takes
-// the rescaling path; every other chunk costs one fma, one clamp, one exp2,
-// one add and one fma per element.
-// Lowest index in the chunk of an element equal to v (some lane holds one):
-// the first load k with a match, its lowest lane, that lane's lowest element.
-template <int U, int VEC, typename IdxF>
-__device__ __forceinline__ int first_index_of(const float (&x)[U * VEC], float v, IdxF idx_of) {
-#pragma unroll
-  for (int k = 0; k < U; ++k) {
-    uint64_t m[VEC], lanes = 0;
-#pragma unroll
-    for (int j = 0; j < VEC; ++j) {
-      m[j] = __builtin_amdgcn_ballot_w64(x[k * VEC + j] == v);
-      lanes |= m[j];
-    }
-    if (lanes != 0) {
-      const int ln = __builtin_ctzll(lanes);
-      int jj = 0;
-#pragma unroll
-      for (int j = VEC - 1; j >= 0; --j)
-        if ((m[j] >> ln) & 1ull) jj = j;
-      return idx_of(k, jj, ln);
-    }
-  }
-  return kIdxNone;
-}
-
-// ANY_ORDER: chunks may arrive in any index order, so a chunk that ties the
-// maximum can still hold its first occurrence.
-template <int U, int VEC, bool ANY_ORDER, typename IdxF>
-__device__ __forceinline__ void chunk_update(WaveState &st, const float (&x)[U * VEC],
-                                             IdxF idx_of) {
-  constexpr int CH = U * VEC;
-  float cm = x[0];
-#pragma unroll
-  for (int e = 1; e < CH; ++e) cm = fmaxf(cm, x[e]);
-  if (__builtin_amdgcn_ballot_w64(cm > st.M) != 0) {
-    // The wave maximum rises (about ln(#chunks) times per wave): rescale,
-    // demote the old maximal element into the uniform extra sums, and exclude
-    // the new maximal elements from z (one of them stays out; the others are
-    // ties and re-enter through zx).  Counting and locating them runs on the
-    // scalar unit from ballots.
-    const float cmw = wave_max(cm);
-    const float Rn = cmw * kLog2e;
-    if (st.M != -kInf) {
-      const float delta = st.R - Rn;
-      const float f = __builtin_amdgcn_exp2f(delta);
-      st.S = f * fmaf(delta, st.z, st.S);
-      st.z = st.z * f;
-      const float e0 = fmaf(st.M, kLog2e, -st.R);      // exact residual
-      const float w0 = __builtin_amdgcn_exp2f(e0);
-      const float zx1 = st.zx + w0;
-      st.Sx = f * fmaf(delta, zx1, fmaf(w0, e0, st.Sx));
-      st.zx = zx1 * f;
-    }
-    st.M = cmw;
-    st.R = Rn;
-    int cnt = 0, first = kIdxNone;
-#pragma unroll
-    for (int k = 0; k < U; ++k) {
-      uint64_t lanes = 0;
-      uint64_t m[VEC];
-#pragma unroll
-      for (int j = 0; j < VEC; ++j) {
-        const float xv = x[k * VEC + j];
-        const bool eq = xv == cmw;
-        m[j] = __builtin_amdgcn_ballot_w64(eq);
-        cnt += __builtin_popcountll(m[j]);
-        lanes |= m[j];
-        const float d = clamp_d(fmaf(xv, kLog2e, -Rn));
-        const float t = eq ? 0.0f : __builtin_amdgcn_exp2f(d);
-        st.z += t;
-        st.S = fmaf(t, d, st.S);
-      }
-      if (first == kIdxNone && lanes != 0) {
-        const int ln = __builtin_ctzll(lanes);
-        int jj = 0;
-#pragma unroll
-        for (int j = VEC - 1; j >= 0; --j)
-          if ((m[j] >> ln) & 1ull) jj = j;
-        first = idx_of(k, jj, ln);
-      }
-    }
-    st.idx = first;
-    if (cnt > 1) {
-      // ties of the new maximum weigh 2^e1 against R
-      const float e1 = fmaf(cmw, kLog2e, -Rn);
-      const float w1 = (float)(cnt - 1) * __builtin_amdgcn_exp2f(e1);
-      st.zx += w1;
-      st.Sx = fmaf(w1, e1, st.Sx);
-    }
-  } else if (st.M != -kInf) {
-    const float nR = -st.R;
-#pragma unroll
-    for (int e = 0; e < CH; ++e) {
-      const float d = clamp_d(fmaf(x[e], kLog2e, nR));
-      const float t = __builtin_amdgcn_exp2f(d);
-      st.z += t;
-      st.S = fmaf(t, d, st.S);
-    }
-    if constexpr (ANY_ORDER) {
-      if (__builtin_amdgcn_ballot_w64(cm == st.M) != 0)
-        st.idx = min(st.idx, first_index_of<U, VEC>(x, st.M, idx_of));
-    }
-  }
-}
-
-// Wave sums against R -> weights relative to M (exact residual e = M log2e - R:
-// 2^(x log2e - M log2e) = 2^(x log2e - R) 2^-e).  A reference that overflowed
-// (|M| > 2^127 / log2 e) poisons z so the row takes the two-pass path.
-__device__ __forceinline__ void to_max_relative(const WaveState &st, float &z, float &S) {
-  if (st.M == -kInf) return;
-  if (!bits_finite(__float_as_uint(st.R))) { z = __builtin_nanf(""); return; }
-  const float e = fmaf(st.M, kLog2e, -st.R);
-  const float g = __builtin_amdgcn_exp2f(-e);
-  S = g * fmaf(-e, z, S);
-  z = g * z;
-}
-
-// Merge partial b into a (a, b relative to their own maxima).
-__device__ __forceinline__ void merge_partial(Partial &a, const Partial &b) {
-  if (b.M == -kInf) return;
-  if (a.M == -kInf) {
-    const float sb = a.sb; const int ib = a.ib; const float xb = a.xb;
-    a = b;
-    // sampling fields merge separately below
-    a.sb = sb; a.ib = ib; a.xb = xb;
-  } else {
-    Partial w = a, o = b;
-    if (b.M > a.M || (b.M == a.M && b.idx < a.idx)) { w = b; o = a; }
-    const float delta = (o.M - w.M) * kLog2e;
-    const float f = __builtin_amdgcn_exp2f(delta);
-    const float zo = 1.0f + o.z;
-    const float z = w.z + zo * f;
-    const float S = w.S + f * fmaf(delta, zo, o.S);
-    const float sb = a.sb; const int ib = a.ib; const float xb = a.xb;
-    a = w;
-    a.z = z;
-    a.S = S;
-    a.sb = sb; a.ib = ib; a.xb = xb;
-  }
-}
-__device__ __forceinline__ void merge_sample(Partial &a, const Partial &b) {
-  if (b.sb > a.sb || (b.sb == a.sb && b.ib < a.ib)) { a.sb = b.sb; a.ib = b.ib; a.xb = b.xb; }
-}
-
-__device__ __forceinline__ bool is_suppressed(const StatsArgs &a, int64_t v) {
-  for (int i = 0; i < a.n_suppress; ++i)
-    if (a.suppress[i] == v) return true;
-  return false;
-}
-
-__device__ __forceinline__ float gumbel_at(const StatsArgs &a, uint32_t b, uint32_t l, int64_t v) {
-  const Philox4 p = philox4x32_10((uint32_t)(v >> 2), l, b, a.step, a.key0, a.key1);
-  return gumbel_from_word(p.w[v & 3]);
-}
-
-// Stream [lo, hi) of one row.  VECLOAD: 16-byte loads (row start 16-byte
-// aligned, lo/hi multiples of VEC).  Full workgroup iterations run without
-// bounds checks, with the next iteration's loads in flight while the current
-// one is reduced; one masked iteration finishes the slice.  The workgroup's
-// partial lands in *out (valid in thread 0).
-template <typename T, int NT, int UV, bool SAMPLE, bool VECLOAD>
-__device__ void stream_slice(const StatsArgs &a, const T *row, int64_t lo, int64_t hi,
-                             uint32_t b, uint32_t l, Partial *wave_parts, Partial *out) {
-  using E = ElemT<T>;
-  constexpr int VEC = VECLOAD ? E::VEC : 1;
-  constexpr int U = VECLOAD ? UV : 8;
-  constexpr int CH = VEC * U;
-  constexpr int STEP = NT * CH;                 // elements per workgroup iteration
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
-  WaveState st;
-  st.M = -kInf; st.R = -kInf; st.idx = kIdxNone; st.zx = 0.f; st.Sx = 0.f; st.z = 0.f; st.S = 0.f;
-  st.sb = -kInf; st.ib = kIdxNone; st.xb = -kInf;
-  // Greedy rows sweep their full iterations starting at a row-dependent one
-  // (rows lie a power of two apart, and rows swept in lockstep would all
-  // press on the same HBM channels); the sampled path keeps index order.
-  constexpr bool ROTATE = VECLOAD && !SAMPLE;
-  int sp = 0;          // next suppress id not below the current iteration
-  int64_t sp_base = lo;
-
-  auto process = [&](float (&x)[CH], int64_t base) {
-    // suppress ids inside this iteration (rare, workgroup-uniform test); the
-    // bases ascend except where a rotated sweep wraps around
-    if (base < sp_base) sp = 0;
-    sp_base = base;
-    while (sp < a.n_suppress && a.suppress[sp] < base) ++sp;
-    if (sp < a.n_suppress && a.suppress[sp] < base + STEP) {
-      for (int q = sp; q < a.n_suppress && a.suppress[q] < base + STEP; ++q) {
-        // element (k, thread, e) of the iteration holds base + (k NT + thread) VEC + e;
-        // the owner and slot are uniform, so x stays in registers
-        const int off = (int)(a.suppress[q] - base);
-        const int ks = off / (NT * VEC), rs = off - ks * (NT * VEC);
-        const int owner = rs / VEC, es = rs - owner * VEC;
-        if (tid == owner) {
-#pragma unroll
-          for (int k = 0; k < U; ++k)
-#pragma unroll
-            for (int e = 0; e < VEC; ++e)
-              if (k == ks && e == es) x[k * VEC + e] = -kInf;
-        }
-      }
-    }
-    if constexpr (SAMPLE) {
-#pragma unroll
-      for (int k = 0; k < U; ++k) {
-        const int64_t v0 = base + (int64_t)(k * NT + tid) * VEC;
-        if constexpr (VEC >= 4) {
-#pragma unroll
-          for (int q = 0; q < VEC / 4; ++q) {
-            const int64_t vq = v0 + 4 * q;
-            const Philox4 p = philox4x32_10((uint32_t)(vq >> 2), l, b, a.step, a.key0, a.key1);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float xv = x[k * VEC + 4 * q + j];
-              const float sc = fmaf(xv, a.inv_temp, gumbel_from_word(p.w[j]));
-              if (sc > st.sb) { st.sb = sc; st.ib = (int)(vq + j); st.xb = xv; }
-            }
-          }
-        } else {
-          const float xv = x[k];
-          if (v0 < hi) {
-            const float sc = fmaf(xv, a.inv_temp, gumbel_at(a, b, l, v0));
-            if (sc > st.sb) { st.sb = sc; st.ib = (int)v0; st.xb = xv; }
-          }
-        }
-      }
-    }
-    chunk_update<U, VEC, ROTATE>(st, x, [&](int k, int j, int ln) -> int {
-      return (int)(base + (int64_t)(k * NT + wave * 64 + ln) * VEC + j);
-    });
-  };
-
-  float x[CH];
-  if constexpr (VECLOAD) {
-    constexpr int64_t ITER = STEP / VEC;          // uint4 per workgroup iteration
-    const int64_t n_full = (hi - lo) / STEP;
-    const uint4 *p = reinterpret_cast<const uint4 *>(row + lo) + tid;
-    // Two register buffers in turn: the loads of iteration i + 1 are in flight
-    // while iteration i is reduced, and no buffer is ever copied.
-    const int64_t it0 = (ROTATE && n_full > 1) ? ((int64_t)b * a.L + l) % n_full : 0;
-    auto rot = [&](int64_t it) {
-      const int64_t j = it + it0;
-      return j >= n_full ? j - n_full : j;
-    };
-    auto load = [&](uint4 (&r)[U], int64_t it) {
-      it = rot(it);
-      const uint4 *q = p + it * ITER;
-#pragma unroll
-      for (int k = 0; k < U; ++k) r[k] = load_stream(q + k * NT);
-    };
-    auto run = [&](const uint4 (&r)[U], int64_t it) {
-      it = rot(it);
-#pragma unroll
-      for (int k = 0; k < U; ++k)
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) x[k * VEC + e] = E::at(r[k], e);
-      process(x, lo + it * STEP);
-    };
-    if (n_full > 0) {
-      uint4 ba[U], bb[U];
-      load(ba, 0);
-      int64_t it = 0;
-      for (; it + 2 < n_full; it += 2) {
-        load(bb, it + 1);
-        run(ba, it);
-        load(ba, it + 2);
-        run(bb, it + 1);
-      }
-      if (it + 1 < n_full) {
-        load(bb, it + 1);
-        run(ba, it);
-        run(bb, it + 1);
-      } else {
-        run(ba, it);
-      }
-    }
-    const int64_t tb = lo + n_full * STEP;
-    if (tb < hi) {
-#pragma unroll
-      for (int k = 0; k < U; ++k) {
-        const int64_t v0 = tb + (int64_t)(k * NT + tid) * VEC;
-        if (v0 < hi) {
-          const uint4 r = load_stream(reinterpret_cast<const uint4 *>(row + v0));
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) x[k * VEC + e] = E::at(r, e);
-        } else {
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) x[k * VEC + e] = -kInf;
-        }
-      }
-      process(x, tb);
-    }
-  } else {
-    for (int64_t base = lo; base < hi; base += STEP) {
-#pragma unroll
-      for (int k = 0; k < U; ++k) {
-        const int64_t v = base + (int64_t)(k * NT + tid);
-        x[k] = (v < hi) ? E::load1(row + v) : -kInf;
-      }
-      process(x, base);
-    }
-  }
-
-  // Wave partial -> LDS.
-  Partial p;
-  p.M = st.M;
-  p.idx = st.idx;
-  p.z = wave_sum(st.z) + st.zx;
-  p.S = wave_sum(st.S) + st.Sx;
-  to_max_relative(st, p.z, p.S);
-  p.sb = -kInf; p.ib = kIdxNone; p.xb = -kInf; p.pad = 0;
-  if constexpr (SAMPLE) {
-    // first-best over the lanes: max score, lowest index on ties
-    float sb = st.sb; int ib = st.ib; float xb = st.xb;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float osb = __shfl_xor(sb, off);
-      const int oib = __shfl_xor(ib, off);
-      const float oxb = __shfl_xor(xb, off);
-      if (osb > sb || (osb == sb && oib < ib)) { sb = osb; ib = oib; xb = oxb; }
-    }
-    p.sb = sb; p.ib = ib; p.xb = xb;
-  }
-  if (lane == 0) wave_parts[wave] = p;
-  __syncthreads();
-  if (tid == 0) {
-    Partial acc = wave_parts[0];
-    for (int w = 1; w < NT / 64; ++w) {
-      merge_partial(acc, wave_parts[w]);
-      if constexpr (SAMPLE) merge_sample(acc, wave_parts[w]);
-    }
-    *out = acc;
-  }
-}
-
-struct RowResult { int x0; float prob; float ent; };
-
-// Plain two-pass recomputation of a degenerate row (NaN, +inf, or no finite
-// unsuppressed logit), with the limit semantics of the header.  Every thread
-// of the workgroup calls it; the result is valid in thread 0.
-template <typename T, int NT, bool SAMPLE>
-__device__ RowResult slow_row(const StatsArgs &a, const T *row, uint32_t b, uint32_t l,
-                              unsigned char *scratch) {
-  using E = ElemT<T>;
-  const int tid = threadIdx.x;
-  float *fs = reinterpret_cast<float *>(scratch);          // [NT]
-  int *is = reinterpret_cast<int *>(scratch) + NT;         // [NT]
-  int *js = reinterpret_cast<int *>(scratch) + 2 * NT;     // [NT]
-  float *gs = reinterpret_cast<float *>(scratch) + 3 * NT; // [NT]
-  const int64_t V = a.V;
-  // pass 1: max (NaN -> -inf), its first index, number and first index of +inf
-  float m = -kInf; int im = kIdxNone; int ninf = 0; int iinf = kIdxNone;
-  for (int64_t v = tid; v < V; v += NT) {
-    if (is_suppressed(a, v)) continue;
-    float x = E::load1(row + v);
-    if (x != x) x = -kInf;
-    if (x > m) { m = x; im = (int)v; }
-    if (x == kInf) { ++ninf; if (iinf == kIdxNone) iinf = (int)v; }
-  }
-  fs[tid] = m; is[tid] = im; js[tid] = ninf; gs[tid] = __int_as_float(iinf);
-  __syncthreads();
-  __shared__ float s_m;
-  __shared__ int s_im, s_ninf, s_iinf;
-  if (tid == 0) {
-    float M = -kInf; int IM = kIdxNone; int N = 0; int II = kIdxNone;
-    for (int t = 0; t < NT; ++t) {
-      if (fs[t] > M || (fs[t] == M && is[t] < IM)) { M = fs[t]; IM = is[t]; }
-      N += js[t];
-      II = min(II, __float_as_int(gs[t]));
-    }
-    s_m = M; s_im = IM; s_ninf = N; s_iinf = II;
-  }
-  __syncthreads();
-  const float M = s_m;
-  const int nA = (int)V - a.n_suppress;
-  const bool finite = bits_finite(__float_as_uint(M));
-  // pass 2: sums relative to M excluding the first maximal element (finite M),
-  // and the sampled argmax over the relevant support.
-  float z = 0.f, S = 0.f, sb = -kInf, xb = -kInf; int ib = kIdxNone;
-  for (int64_t v = tid; v < V; v += NT) {
-    if (is_suppressed(a, v)) continue;
-    float x = E::load1(row + v);
-    if (x != x) x = -kInf;
-    if (finite) {
-      if (v != s_im) {
-        const float d = (x - M) * kLog2e;
-        const float t = __builtin_amdgcn_exp2f(d);
-        z += t;
-        if (t > 0.f) S = fmaf(t, d, S);
-      }
-      if (SAMPLE) {
-        const float s = fmaf(x, a.inv_temp, gumbel_at(a, b, l, v));
-        if (s > sb) { sb = s; ib = (int)v; xb = x; }
-      }
-    } else if (SAMPLE) {
-      const bool in_support = (M == -kInf) ? true : (x == kInf);
-      if (in_support) {
-        const float g = gumbel_at(a, b, l, v);
-        if (g > sb) { sb = g; ib = (int)v; xb = x; }
-      }
-    }
-  }
-  __syncthreads();
-  fs[tid] = z; gs[tid] = S; is[tid] = ib; js[tid] = __float_as_int(sb);
-  float *xs = reinterpret_cast<float *>(scratch) + 4 * NT;
-  xs[tid] = xb;
-  __syncthreads();
-  RowResult r;
-  r.x0 = 0; r.prob = 0.f; r.ent = 0.f;
-  if (tid == 0) {
-    float Z = 0.f, SS = 0.f, SB = -kInf, XB = -kInf; int IB = kIdxNone;
-    for (int t = 0; t < NT; ++t) {
-      Z += fs[t];
-      SS += gs[t];
-      const float s = __int_as_float(js[t]);
-      if (s > SB || (s == SB && is[t] < IB)) { SB = s; IB = is[t]; XB = xs[t]; }
-    }
-    if (finite) {
-      r.ent = log1pf(Z) - kLn2 * SS / (1.0f + Z);
-      if (SAMPLE) {
-        r.x0 = IB;
-        r.prob = __builtin_amdgcn_exp2f((XB - M) * kLog2e) / (1.0f + Z);
-      } else {
-        r.x0 = s_im;
-        r.prob = 1.0f / (1.0f + Z);
-      }
-    } else if (M == -kInf) {
-      r.x0 = SAMPLE ? IB : a.first_allowed;
-      r.prob = 1.0f / (float)nA;
-      r.ent = logf((float)nA);
-    } else {
-      r.x0 = SAMPLE ? IB : s_iinf;
-      r.prob = 1.0f / (float)s_ninf;
-      r.ent = logf((float)s_ninf);
-    }
-  }
-  return r;
-}
-
-// Does any fused rule look at this row?
-__device__ __forceinline__ bool row_needed(const StatsArgs &a, int64_t row_id) {
-  bool need = a.has_edit && a.edit_mask[row_id];
-  for (int r = 0; r < a.n_rank_rules; ++r) need = need || a.rank_rules[r].mask[row_id];
-  return need;
-}
-
-// Statistics of a finished row from its merged partial; false when the row is
-// degenerate (NaN, +inf, or no finite unsuppressed logit) and needs the
-// two-pass path.
-template <bool SAMPLE>
-__device__ __forceinline__ bool finalize_partial(const Partial &p, RowResult &res) {
-  const bool ok = bits_finite(__float_as_uint(p.M)) && bits_finite(__float_as_uint(p.z)) &&
-                  bits_finite(__float_as_uint(p.S)) &&
-                  (!SAMPLE || (p.ib != kIdxNone && bits_finite(__float_as_uint(p.sb))));
-  if (ok) {
-    const float zf = 1.0f + p.z;
-    res.ent = log1pf(p.z) - kLn2 * p.S / zf;
-    if (SAMPLE) {
-      res.x0 = p.ib;
-      res.prob = __builtin_amdgcn_exp2f((p.xb - p.M) * kLog2e) / zf;
-    } else {
-      res.x0 = p.idx;
-      res.prob = 1.0f / zf;
-    }
-  }
-  return ok;
-}
-
-// Writes one row's statistics (coherent: the batch-row finisher and the
-// rules read them) and decides its edit; returns 1 if the row was edited.
-__device__ __forceinline__ int publish_row(const StatsArgs &a, int64_t row_id,
-                                           const RowResult &res) {
-  store_coherent(&a.x0[row_id], res.x0);
-  store_coherent(&a.prob[row_id], res.prob);
-  store_coherent(&a.entropy[row_id], res.ent);
-  if (!a.has_edit) return 0;
-  const uint8_t e = edit_decision(a.edit_mask[row_id], res.x0, a.edit_tokens[row_id],
-                                  res.prob, a.edit_tau);
-  a.edit_out[row_id] = e;
-  if (e && a.canvas) a.canvas[row_id] = res.x0;      // this row's own token
-  return e;
-}
-
-// Canvas update for the committed positions of batch row b and its counts.
-// Runs in the workgroup that completed the batch row, after the rank rule
-// (whose output this workgroup has just written).  edits < 0: the edit count
-// is in the workspace.
-__device__ inline void finish_canvas(const StatsArgs &a, uint32_t b, int edits) {
-  __shared__ int s_left[16];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
-  const int64_t L = a.L, base = (int64_t)b * L;
-  int left = 0;
-  if (a.n_rank_rules) {
-    const RuleDev &r = a.rank_rules[0];
-    for (int64_t l = tid; l < L; l += blockDim.x) {
-      const bool committed = r.out[base + l] != 0;
-      if (committed && a.canvas) a.canvas[base + l] = load_coh(&a.x0[base + l]);
-      left += (r.mask[base + l] && !committed) ? 1 : 0;
-    }
-  }
-  if (a.counts) {
-    const int w = wave_sum_i(left);
-    if (lane == 0) s_left[wave] = w;
-    __syncthreads();
-    if (tid == 0) {
-      int tot = 0;
-      for (int i = 0; i < nw; ++i) tot += s_left[i];
-      if (edits < 0) {
-        edits = (int)load_coh(&a.edit_count[b]);
-        a.edit_count[b] = 0u;        // leave the workspace zeroed
-      }
-      a.counts[2 * b] = tot;
-      a.counts[2 * b + 1] = edits;
-    }
-  }
-}
-
-// The batch row's statistics are all published: rank rules, canvas, counts.
-__device__ inline void complete_batch_row(const StatsArgs &a, uint32_t b, unsigned char *smem,
-                                          int edits) {
-  for (int r = 0; r < a.n_rank_rules; ++r)
-    run_batch_rule(a.rank_rules[r], (int)b, (int)a.L, a.prob, a.entropy, smem);
-  if (a.canvas || a.counts) finish_canvas(a, b, edits);
-  if (threadIdx.x == 0) a.batch_count[b] = 0u;   // leave the workspace zeroed
-}
-
-// Whole rows: after a row's statistics are published, count the row into its
-// batch row; the workgroup that completes the batch row runs the rank rules on
-// the statistics the launch has just written (coherent loads), then the canvas
-// update and the counts.
-__device__ inline void finish_row(const StatsArgs &a, uint32_t b, unsigned char *smem) {
-  __shared__ int s_last;
-  const int tid = threadIdx.x;
-  if (!a.need_batch) return;
-  if (tid == 0) {
-    wait_stores_complete();
-    const uint32_t prev = atomicAdd(&a.batch_count[b], 1u);
-    s_last = (prev == (uint32_t)(a.L - 1));
-  }
-  __syncthreads();
-  if (!s_last) return;
-  complete_batch_row(a, b, smem, -1);
-}
-
-template <typename T, int NT, int UV, bool SAMPLE, bool VECLOAD>
-__global__ __launch_bounds__(NT) void token_stats_kernel(StatsArgs a) {
-  extern __shared__ __align__(16) unsigned char smem[];   // slice partials, then the rules
-  __shared__ Partial wave_parts[NT / 64];
-  __shared__ Partial slice_parts_acc;
-  __shared__ int s_flag;
-  __shared__ __align__(16) unsigned char slow_scratch[5 * NT * 4];
-
-  const int tid = threadIdx.x;
-  const int64_t wg = blockIdx.x;
-  const int64_t row_id = wg / a.slices;
-  const int slice = (int)(wg - row_id * a.slices);
-  const uint32_t b = (uint32_t)(row_id / a.L), l = (uint32_t)(row_id - (int64_t)b * a.L);
-  const T *row = reinterpret_cast<const T *>(a.logits) + row_id * a.row_stride;
-  const int64_t lo = (int64_t)slice * a.slice_len;
-  const int64_t hi = min(lo + a.slice_len, a.V);
-
-  // Candidate-row skipping: a row that no rule looks at is not read, and its
-  // statistics are left as they were; an edit rule's output for it is 0.
-  // Slice 0 still counts it into its batch row.
-  if (a.skip_rows && !row_needed(a, row_id)) {
-    if (slice != 0) return;
-    if (tid == 0 && a.has_edit) a.edit_out[row_id] = 0;
-    finish_row(a, b, smem);
-    return;
-  }
-
-  stream_slice<T, NT, UV, SAMPLE, VECLOAD>(a, row, lo, hi, b, l, wave_parts, &slice_parts_acc);
-
-  // Split rows: publish the slice partial and count it on the row's own
-  // counter (a counter per row keeps the atomics of a launch spread out); the
-  // last slice to arrive fetches every slice's partial at once into LDS and
-  // merges them in slice order.
-  if (a.slices > 1) {
-    Partial *parts = &a.partials[row_id * a.slices];
-    if (tid == 0) {
-      store_partial(&parts[slice], slice_parts_acc);
-      wait_stores_complete();
-      const uint32_t prev = atomicAdd(&a.row_count[row_id], 1u);
-      s_flag = (prev == (uint32_t)(a.slices - 1));
-    }
-    __syncthreads();
-    if (!s_flag) return;
-    Partial *lds = reinterpret_cast<Partial *>(smem);    // [slices], before the rules use it
-    for (int s = tid; s < a.slices; s += NT) {
-      lds[s] = load_partial(&parts[s]);
-      uint4 *w = reinterpret_cast<uint4 *>(&parts[s]);   // leave the record zero-filled
-      w[0] = make_uint4(0u, 0u, 0u, 0u);
-      w[1] = make_uint4(0u, 0u, 0u, 0u);
-    }
-    __syncthreads();
-    if (tid == 0) {
-      Partial acc = lds[0];
-      for (int s = 1; s < a.slices; ++s) {       // fixed slice order: reproducible
-        merge_partial(acc, lds[s]);
-        if (SAMPLE) merge_sample(acc, lds[s]);
-      }
-      slice_parts_acc = acc;
-      a.row_count[row_id] = 0u;
-    }
-    __syncthreads();
-  }
-
-  // Finalize the row.
-  __shared__ int s_slow;
-  RowResult res;
-  res.x0 = 0; res.prob = 0.f; res.ent = 0.f;
-  if (tid == 0) s_slow = !finalize_partial<SAMPLE>(slice_parts_acc, res);
-  __syncthreads();
-  if (s_slow) res = slow_row<T, NT, SAMPLE>(a, row, b, l, slow_scratch);
-  if (tid == 0 && publish_row(a, row_id, res) && a.counts) atomicAdd(&a.edit_count[b], 1u);
-  finish_row(a, b, smem);
-}
 
 // ---------------------------------------------------------------- host side
 
 namespace {
-
-struct Plan {
-  int nt;
-  int slices;
-  int64_t slice_len;
-  bool vec;
-};
 
 Plan make_plan(int dtype, int64_t rows, int64_t V, int64_t row_stride, const void *logits) {
   const int esz = dtype == DLLM_BF16 ? 2 : 4;
@@ -815,10 +20,10 @@ Plan make_plan(int dtype, int64_t rows, int64_t V, int64_t row_stride, const voi
   Plan p;
   p.vec = ((uintptr_t)logits % 16 == 0) && ((row_stride * esz) % 16 == 0) && (V % vecn == 0);
   const int cus = device_cu_count();
-  // Enough waves to cover HBM latency: aim for >= 16 waves per CU.
-  // Enough waves per CU to cover HBM latency: many rows -> 256-thread groups,
-  // a few long rows -> 512-thread groups (measured best on the 256 x 262144
-  // canvas: 8 waves per CU with one 16-byte-load chunk in flight each).
+  // Many rows -> 256-thread groups; a few long rows -> 512-thread groups
+  // (measured best on the 256 x 262144 canvas, one row per CU: 8 waves with
+  // one 16-byte-load chunk in flight each; more waves or slices per row
+  // streamed slower).
   if (rows >= 4LL * cus || V < 16384) p.nt = 256;
   else p.nt = 512;
   p.slices = 1;
@@ -851,15 +56,7 @@ size_t workspace_bytes_for(int64_t B, int64_t L, int slices) {
 template <typename T, int NT, int UV>
 hipError_t launch_t(const Plan &p, const StatsArgs &a, int64_t rows, bool sample, size_t smem,
                     hipStream_t s) {
-  dim3 grid((unsigned)(rows * p.slices)), block(NT);
-  if (sample) {
-    if (p.vec) token_stats_kernel<T, NT, UV, true, true><<<grid, block, smem, s>>>(a);
-    else token_stats_kernel<T, NT, UV, true, false><<<grid, block, smem, s>>>(a);
-  } else {
-    if (p.vec) token_stats_kernel<T, NT, UV, false, true><<<grid, block, smem, s>>>(a);
-    else token_stats_kernel<T, NT, UV, false, false><<<grid, block, smem, s>>>(a);
-  }
-  return hipGetLastError();
+  return launch_f<T, NT, UV, false>(p, a, rows, sample, smem, s);
 }
 
 // Dispatch on the plan's (threads, loads per chunk).
@@ -894,7 +91,8 @@ namespace {
 int stats_step(const char *who, const void *logits, int dtype, int64_t B, int64_t L, int64_t V,
                int64_t row_stride, float temperature, uint64_t seed, uint64_t step,
                const int32_t *suppress_ids, int n_suppress, int32_t *x0, float *prob,
-               float *entropy, const dllm_rule *rules, int n_rules, const dllm_canvas *canvas,
+               float *entropy, float *margin, const dllm_rule *rules, int n_rules,
+               const dllm_canvas *canvas,
                void *workspace, size_t workspace_bytes, hipStream_t stream) {
   if (dtype != DLLM_F32 && dtype != DLLM_BF16)
     return fail(DLLM_ERR_DTYPE, "%s: dtype %d is neither DLLM_F32 nor DLLM_BF16", who, dtype);
@@ -944,6 +142,7 @@ int stats_step(const char *who, const void *logits, int dtype, int64_t B, int64_
     seen[r.kind] = true;
     outs[i] = r.out;
     if (r.out == (const void *)x0 || r.out == (const void *)prob || r.out == (const void *)entropy ||
+        (margin && r.out == (const void *)margin) ||
         r.out == (const void *)r.mask || r.out == (const void *)logits)
       return fail(DLLM_ERR_ARG, "%s: rules[%d].out aliases another array", who, i);
     if (r.kind == DLLM_RULE_EDIT) {
@@ -964,6 +163,8 @@ int stats_step(const char *who, const void *logits, int dtype, int64_t B, int64_
                     (long long)L, DLLM_MAX_L);
       const int rc = prepare_rule(r, a.rank_rules[a.n_rank_rules], B, L, who);
       if (rc != DLLM_OK) return rc;
+      if (r.score == DLLM_SCORE_MARGIN && !margin)
+        return fail(DLLM_ERR_ARG, "%s: a rule ranks by margin but the margin output is NULL", who);
       ++a.n_rank_rules;
     }
   }
@@ -972,7 +173,7 @@ int stats_step(const char *who, const void *logits, int dtype, int64_t B, int64_
   if (canvas) {
     if (a.n_rank_rules > 1)
       return fail(DLLM_ERR_ARG, "%s: a canvas step takes at most one ranking rule", who);
-    const void *arrays[] = {logits, x0, prob, entropy, outs[0], outs[1]};
+    const void *arrays[] = {logits, x0, prob, entropy, margin, outs[0], outs[1]};
     for (const void *q : arrays)
       if (q && (q == (const void *)canvas->tokens || q == (const void *)canvas->counts))
         return fail(DLLM_ERR_ARG, "%s: canvas tokens or counts alias another array", who);
@@ -1019,12 +220,14 @@ int stats_step(const char *who, const void *logits, int dtype, int64_t B, int64_
   a.x0 = x0;
   a.prob = prob;
   a.entropy = entropy;
+  a.margin = margin;
 
   const bool sample = temperature > 0.0f;
   size_t smem = a.n_rank_rules ? rule_smem_bytes((int)L, p.nt) : 0;
   if (p.slices > 1) smem = std::max(smem, (size_t)p.slices * sizeof(Partial));
   hipError_t e;
-  if (dtype == DLLM_BF16) e = launch_plan<uint16_t>(p, a, rows, sample, smem, stream);
+  if (a.skip_rows || a.margin) e = launch_full(dtype, p, a, rows, sample, smem, stream);
+  else if (dtype == DLLM_BF16) e = launch_plan<uint16_t>(p, a, rows, sample, smem, stream);
   else e = launch_plan<float>(p, a, rows, sample, smem, stream);
   if (e != hipSuccess)
     return fail(DLLM_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
@@ -1036,22 +239,22 @@ int stats_step(const char *who, const void *logits, int dtype, int64_t B, int64_
 extern "C" int dllm_token_stats(const void *logits, int dtype, int64_t B, int64_t L, int64_t V,
                                 int64_t row_stride, float temperature, uint64_t seed,
                                 uint64_t step, const int32_t *suppress_ids, int n_suppress,
-                                int32_t *x0, float *prob, float *entropy,
+                                int32_t *x0, float *prob, float *entropy, float *margin,
                                 const dllm_rule *rules, int n_rules, void *workspace,
                                 size_t workspace_bytes, hipStream_t stream) {
   return stats_step("dllm_token_stats", logits, dtype, B, L, V, row_stride, temperature, seed,
-                    step, suppress_ids, n_suppress, x0, prob, entropy, rules, n_rules, nullptr,
-                    workspace, workspace_bytes, stream);
+                    step, suppress_ids, n_suppress, x0, prob, entropy, margin, rules, n_rules,
+                    nullptr, workspace, workspace_bytes, stream);
 }
 
 extern "C" int dllm_commit_step(const void *logits, int dtype, int64_t B, int64_t L, int64_t V,
                                 int64_t row_stride, float temperature, uint64_t seed,
                                 uint64_t step, const int32_t *suppress_ids, int n_suppress,
-                                int32_t *x0, float *prob, float *entropy,
+                                int32_t *x0, float *prob, float *entropy, float *margin,
                                 const dllm_rule *rules, int n_rules, const dllm_canvas *canvas,
                                 void *workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!canvas) return fail(DLLM_ERR_ARG, "dllm_commit_step: canvas is NULL");
   return stats_step("dllm_commit_step", logits, dtype, B, L, V, row_stride, temperature, seed,
-                    step, suppress_ids, n_suppress, x0, prob, entropy, rules, n_rules, canvas,
-                    workspace, workspace_bytes, stream);
+                    step, suppress_ids, n_suppress, x0, prob, entropy, margin, rules, n_rules,
+                    canvas, workspace, workspace_bytes, stream);
 }

@@ -91,7 +91,14 @@ int prepare_rule(const dllm_rule &r, RuleDev &d, int64_t B, int64_t L, const cha
   d.k = r.k;
   d.tokens = r.tokens;
   d.param = r.param;
+  d.score = r.score;
+  d.negate = r.score == DLLM_SCORE_NEG_ENTROPY ? 1 : 0;
   if (!r.mask || !r.out) return fail(DLLM_ERR_ARG, "%s: rule mask and out must be non-NULL", who);
+  if (r.score < DLLM_SCORE_PROB || r.score > DLLM_SCORE_NEG_ENTROPY)
+    return fail(DLLM_ERR_ARG, "%s: rule score %d is not a DLLM_SCORE_*", who, r.score);
+  if (r.score != DLLM_SCORE_PROB && r.kind != DLLM_RULE_THRESHOLD && r.kind != DLLM_RULE_TOPK &&
+      r.kind != DLLM_RULE_FACTOR)
+    return fail(DLLM_ERR_ARG, "%s: only threshold, topk and factor take another score", who);
   if (r.kind == DLLM_RULE_TOPK) {
     if (!r.k) return fail(DLLM_ERR_ARG, "%s: topk needs the k array", who);
     return DLLM_OK;

@@ -66,6 +66,16 @@ enum {
   DLLM_RULE_EDIT = 5
 };
 
+/* The confidence a fused THRESHOLD / TOPK / FACTOR rule ranks by (mojo-dllm
+ * "The GPU path", row statistics paragraph: LLaDA and maskgit_plus use p,
+ * topk_margin p minus the runner-up's probability, Dream the negative
+ * entropy). */
+enum {
+  DLLM_SCORE_PROB = 0,          /* prob */
+  DLLM_SCORE_MARGIN = 1,        /* margin (the margin output must be given) */
+  DLLM_SCORE_NEG_ENTROPY = 2    /* -entropy */
+};
+
 /* One commit rule run inside dllm_token_stats on the statistics it has just
  * computed (same launch).  The result is identical to calling the matching
  * dllm_transfer_* function on dllm_token_stats' outputs.
@@ -78,8 +88,11 @@ enum {
  *   strict  THRESHOLD only: 0 -> conf >= tau, 1 -> conf > tau.
  *   k       TOPK only: (B,) int32 quotas.
  *   tokens  EDIT only: (B, L) int32 current canvas.
- * THRESHOLD / FACTOR / TOPK rank by prob, ENTROPY_BOUND by entropy, EDIT uses
- * x0, prob and tokens. */
+ *   score   THRESHOLD / FACTOR / TOPK: DLLM_SCORE_* (0 = prob); must be 0 for
+ *           the other kinds.
+ * THRESHOLD / FACTOR / TOPK rank by the score (prob by default), ENTROPY_BOUND
+ * by entropy, EDIT uses x0, prob and tokens.  Zero-fill the struct before
+ * setting its fields. */
 typedef struct {
   int kind;
   const uint8_t *mask;
@@ -88,6 +101,7 @@ typedef struct {
   int strict;
   const int32_t *k;
   const int32_t *tokens;
+  int score;
 } dllm_rule;
 
 /* ---------------------------------------------------------------------------
@@ -114,6 +128,11 @@ typedef struct {
  *   prob         (B, L) float32 DEVICE output: softmax(logits)[x0], untempered.
  *   entropy      (B, L) float32 DEVICE output: -sum p log p of softmax(logits)
  *                over the unsuppressed ids (natural log), untempered.
+ *   margin       (B, L) float32 DEVICE output, or NULL: p_(1) - p_(2) of
+ *                softmax(logits) over the unsuppressed ids, the topk_margin
+ *                confidence (the runner-up is the largest logit at any index
+ *                but the first maximal one; a tie gives 0, one unsuppressed id
+ *                gives 1), untempered, whatever x0 is.
  *   rules        HOST array of n_rules (0..2) rules fused into the same launch,
  *                or NULL.  At most one rule of each kind.
  *   workspace    DEVICE scratch of at least dllm_token_stats_workspace_size()
@@ -131,6 +150,7 @@ int dllm_token_stats(const void *logits, int dtype, int64_t B, int64_t L,
                      uint64_t seed, uint64_t step,
                      const int32_t *suppress_ids, int n_suppress,
                      int32_t *x0, float *prob, float *entropy,
+                     float *margin,
                      const dllm_rule *rules, int n_rules,
                      void *workspace, size_t workspace_bytes,
                      hipStream_t stream);
@@ -183,6 +203,7 @@ int dllm_commit_step(const void *logits, int dtype, int64_t B, int64_t L,
                      uint64_t seed, uint64_t step,
                      const int32_t *suppress_ids, int n_suppress,
                      int32_t *x0, float *prob, float *entropy,
+                     float *margin,
                      const dllm_rule *rules, int n_rules,
                      const dllm_canvas *canvas,
                      void *workspace, size_t workspace_bytes,

@@ -30,8 +30,12 @@ def to_dev(arr, dtype=None):
 
 
 def stats_np(st):
+    """(x0, prob, entropy) as numpy arrays, plus margin when it was computed."""
     torch.cuda.synchronize()
-    return st.x0.cpu().numpy(), st.prob.cpu().numpy(), st.entropy.cpu().numpy()
+    out = (st.x0.cpu().numpy(), st.prob.cpu().numpy(), st.entropy.cpu().numpy())
+    if getattr(st, "margin", None) is not None:
+        out = out + (st.margin.cpu().numpy(),)
+    return out
 
 
 def max_rel(a, b):
@@ -42,7 +46,7 @@ def max_rel(a, b):
 
 def assert_stats(gpu, ref, dtype, label, mask=None, x0_exact=True, fields=("prob", "entropy")):
     """Compare (x0, prob, entropy) with the oracle on the positions in mask."""
-    gx, gp, ge = gpu
+    gx, gp, ge = gpu[0], gpu[1], gpu[2]
     rx, rp, re = ref.x0, ref.prob, ref.entropy
     if mask is None:
         mask = np.ones(gx.shape, dtype=bool)
@@ -50,7 +54,10 @@ def assert_stats(gpu, ref, dtype, label, mask=None, x0_exact=True, fields=("prob
     if x0_exact:
         bad = np.flatnonzero((gx != rx) & mask)
         assert bad.size == 0, f"{label}: x0 differs at {bad[:10]}"
-    for name, g, r in (("prob", gp, rp), ("entropy", ge, re)):
+    pairs = [("prob", gp, rp), ("entropy", ge, re)]
+    if "margin" in fields:
+        pairs.append(("margin", gpu[3], ref.margin))
+    for name, g, r in pairs:
         if name not in fields:
             continue
         g, r = g[mask], r[mask]

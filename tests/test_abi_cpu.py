@@ -69,7 +69,7 @@ def test_token_stats_argument_errors(lib):
     def call(dtype=1, B=1, L=1, V=8, stride=8, T=0.0, step=0, sup=None, nsup=0, rules=None,
              nrules=0):
         return lib.dllm_token_stats(fake, dtype, B, L, V, stride, T, 0, step, sup, nsup, fake,
-                                    fake, fake, rules, nrules, fake, 1 << 20, None)
+                                    fake, fake, None, rules, nrules, fake, 1 << 20, None)
 
     assert call(dtype=7) == -2 and "dtype" in _err(lib)
     assert call(B=-1) == -1
@@ -99,6 +99,13 @@ def test_token_stats_argument_errors(lib):
     assert call(rules=rules, nrules=1) == -1 and "NaN" in _err(lib)
     rules[0].param = 0.5
     assert call(L=5000, V=8, rules=rules, nrules=1) == -5
+    rules[0].score = 7
+    assert call(rules=rules, nrules=1) == -1 and "score" in _err(lib)
+    rules[0].score = dc.SCORE_MARGIN                  # ranks by margin, no margin output
+    assert call(rules=rules, nrules=1) == -1 and "margin" in _err(lib)
+    rules[0].kind = dc.RULE_ENTROPY_BOUND             # entropy_bound ranks by entropy only
+    assert call(rules=rules, nrules=1) == -1 and "score" in _err(lib)
+    rules[0].kind, rules[0].score = dc.RULE_THRESHOLD, 0
     # empty shapes: OK with nothing launched
     assert call(B=0) == 0 and call(L=0) == 0
 
@@ -110,7 +117,7 @@ def test_commit_step_argument_errors(lib):
 
     def call(canvas, rules=None, nrules=0, B=1, L=4, V=8):
         return lib.dllm_commit_step(fake, 1, B, L, V, V, 0.0, 0, 0, None, 0, fake, P(24), P(40),
-                                    rules, nrules, canvas, fake, 1 << 20, None)
+                                    None, rules, nrules, canvas, fake, 1 << 20, None)
 
     assert call(None) == -1 and "canvas" in _err(lib)
     cv = dc._CCanvas()
