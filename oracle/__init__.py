@@ -30,6 +30,8 @@ from .rules import (threshold_transfer, topk_transfer, factor_transfer,
                     entropy_bound_transfer, edit_transfer, transfer_schedule,
                     block_ranges, block_causal_mask)
 from .step import commit_step, apply_step, counts, rank_rule, StepResult
+from .uniform import (linear_temperature, uniform_canvas, renoise, StableConfidentStopping,
+                      decode_uniform)
 
 __all__ = [
     "philox4x32_10", "philox_words", "uniform_from_word", "gumbel_noise",
@@ -38,4 +40,6 @@ __all__ = [
     "entropy_bound_transfer", "edit_transfer", "transfer_schedule",
     "block_ranges", "block_causal_mask",
     "commit_step", "apply_step", "counts", "rank_rule", "StepResult",
+    "linear_temperature", "uniform_canvas", "renoise", "StableConfidentStopping",
+    "decode_uniform",
 ]

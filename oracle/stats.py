@@ -23,6 +23,10 @@ Readings of the pages taken here (each also listed in the design doc):
     being the largest logit at any index other than the argmax): p_(1) - p_(2)
     of softmax(logits) over the unsuppressed ids, whatever x0 is; a tie at the
     maximum gives 0, a single unsuppressed id gives 1;
+  * with a statistics temperature Ts (the DiffusionGemma loop of "Uniform-noise
+    decoding (DiffusionGemma)" measures entropy on the temperature-scaled
+    logits z = logits / T), prob, entropy and margin are those of
+    softmax(logits / Ts); x0 does not depend on Ts;
   * "NaN-safe": a NaN logit counts as -inf; a row whose unsuppressed logits are
     all -inf (or NaN) is uniform over the unsuppressed ids; a row with +inf
     logits is uniform over its +inf ids.  These are the limits of finite rows,
@@ -69,11 +73,13 @@ def _first_argmax(values, allowed):
     return int(idx[np.flatnonzero(vals == best)[0]])
 
 
-def token_stats_row(ell, temperature, seed, step, b, l, suppressed):
+def token_stats_row(ell, temperature, seed, step, b, l, suppressed, stats_temperature=1.0):
     """Statistics of one position.
 
     ell: float64 (V,) logits; temperature: the float32 value as float;
-    suppressed: bool (V,) mask of suppressed ids (not all True).
+    suppressed: bool (V,) mask of suppressed ids (not all True);
+    stats_temperature: Ts > 0 (a float32 value as float), prob / entropy /
+    margin are those of softmax(ell / Ts).
     Returns (x0, prob, entropy, margin) as (int, float, float, float).
     """
     V = ell.shape[0]
@@ -85,25 +91,26 @@ def token_stats_row(ell, temperature, seed, step, b, l, suppressed):
     sampling = temperature > 0.0
     g = gumbel_noise(seed, step, b, l, V) if sampling else None
 
-    m = lp[allowed].max()
+    ls = lp / stats_temperature                          # the logits the softmax sees
+    m = ls[allowed].max()
     if np.isfinite(m):
         with np.errstate(invalid="ignore", over="ignore"):
-            w = np.where(allowed, np.exp(lp - m), 0.0)   # exp(-inf) = 0
+            w = np.where(allowed, np.exp(ls - m), 0.0)   # exp(-inf) = 0
         # z = 1 + z_minus, z_minus = the mass of every entry but one maximal one;
         # log z = log1p(z_minus) keeps its accuracy when z_minus is below the
         # float64 resolution of 1 (a top logit some 40+ nats above the rest).
-        top = _first_argmax(lp, allowed)
+        top = _first_argmax(ls, allowed)
         z_minus = np.sum(np.delete(w, top))
         z = 1.0 + z_minus
         log_z = np.log1p(z_minus)
         p = w / z
         keep = allowed & (p > 0.0)
-        H = -np.sum(p[keep] * ((lp[keep] - m) - log_z))
+        H = -np.sum(p[keep] * ((ls[keep] - m) - log_z))
         # runner-up: the largest logit at any allowed index but the top one
         r = -np.inf
         for v in np.flatnonzero(allowed):
-            if v != top and lp[v] > r:
-                r = lp[v]
+            if v != top and ls[v] > r:
+                r = ls[v]
         margin = -np.expm1(r - m) / z                    # (1 - e^(r - m)) / z
         if sampling:
             with np.errstate(invalid="ignore"):
@@ -124,12 +131,14 @@ def token_stats_row(ell, temperature, seed, step, b, l, suppressed):
 
 
 def token_stats(logits, dtype="f32", temperature=0.0, seed=None, step=0,
-                suppress_ids=(), positions=None):
+                suppress_ids=(), positions=None, stats_temperature=1.0):
     """Per-position (x0, prob, entropy, margin) of (B, L, V) logits.
 
     temperature: 0 = greedy; > 0 = Gumbel-max with key ``seed`` at ``step``
     (``seed`` is required then, as the pages require an explicit key).  The
     temperature is taken as the float32 value a C caller would pass.
+    stats_temperature Ts > 0: prob, entropy and margin are those of
+    softmax(logits / Ts), Ts taken as a float32 value too.
     positions: optional iterable of (b, l); then only those are computed and the
     other outputs are left at x0 = -1, prob = entropy = margin = NaN.
     """
@@ -142,6 +151,9 @@ def token_stats(logits, dtype="f32", temperature=0.0, seed=None, step=0,
         raise ValueError("temperature must be >= 0")
     if T > 0.0 and seed is None:
         raise ValueError("sampling needs an explicit seed")
+    Ts = float(np.float32(stats_temperature))
+    if not (Ts > 0.0 and np.isfinite(Ts)):
+        raise ValueError("stats_temperature must be finite and > 0")
     suppressed = np.zeros(V, dtype=bool)
     for s in suppress_ids:
         if not 0 <= int(s) < V:
@@ -155,5 +167,5 @@ def token_stats(logits, dtype="f32", temperature=0.0, seed=None, step=0,
     for b, l in todo:
         row = widen_logits(a[b, l], dtype)
         x0[b, l], prob[b, l], ent[b, l], mar[b, l] = token_stats_row(
-            row, T, seed if seed is not None else 0, step, b, l, suppressed)
+            row, T, seed if seed is not None else 0, step, b, l, suppressed, Ts)
     return Stats(x0, prob, ent, mar)

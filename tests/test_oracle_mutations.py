@@ -15,11 +15,11 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-PIN_FILES = ["test_oracle_pins.py", "test_oracle_step.py"]
+PIN_FILES = ["test_oracle_pins.py", "test_oracle_step.py", "test_oracle_uniform.py"]
 
 MUTATIONS = [
     # (file, original text, mutated text, -k selection of pin tests)
-    ("stats.py", "((lp[keep] - m) - log_z)", "(lp[keep] - m)",
+    ("stats.py", "((ls[keep] - m) - log_z)", "(ls[keep] - m)",
      "moment or two_level or uniform"),
     ("stats.py", "log_z = np.log1p(z_minus)", "log_z = np.log(z)", "peaked"),
     ("stats.py", "H = -np.sum(", "H = np.sum(", "two_level or moment"),
@@ -51,9 +51,19 @@ MUTATIONS = [
     ("rules.py", "start = (P // bl) * bl if align else P", "start = P", "block_ranges"),
     ("rules.py", "and _conf(prob[b, l]) > tau_edit", "and _conf(prob[b, l]) >= tau_edit",
      "edit"),
-    ("stats.py", "if v != top and lp[v] > r:", "if lp[v] > r:", "margin"),
+    ("stats.py", "if v != top and ls[v] > r:", "if ls[v] > r:", "margin"),
     ("stats.py", "margin = -np.expm1(r - m) / z", "margin = (1.0 - np.exp(r - m)) / z", "margin"),
     ("stats.py", "(1.0 if n == 1 else 0.0)", "0.0", "margin"),
+    ("stats.py", "ls = lp / stats_temperature", "ls = lp", "stats_temperature"),
+    ("uniform.py", "return t_min + (t_max - t_min) * remaining / num_steps",
+     "return t_max + (t_min - t_max) * remaining / num_steps", "linear_temperature"),
+    ("uniform.py", "out[b, l] = (x * int(V)) >> 64", "out[b, l] = x % int(V)", "uniform_canvas"),
+    ("uniform.py", "self.count[b] = self.count[b] + 1 if same else 0",
+     "self.count[b] = self.count[b] + 1", "stopping"),
+    ("uniform.py", "confident = total <= Fraction(self.c) * L", "confident = total <= Fraction(self.c)",
+     "stopping"),
+    ("uniform.py", "canvas = np.where(done[:, None], canvas, new_canvas)", "canvas = new_canvas",
+     "freezes_finished"),
     ("step.py", "take = (commit is not None and commit[b, l]) or (edit is not None and edit[b, l])",
      "take = commit is not None and commit[b, l]", "hand_worked"),
     ("step.py", "if cand[b, l] and not commit[b, l])", "if cand[b, l])", "hand_worked or block_loop"),
