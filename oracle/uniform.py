@@ -26,7 +26,8 @@ DESIGN.md):
     draw of token_stats at temperature T (same Philox noise);
   * StableConfidentStopping(k, c): a row counts the consecutive steps whose
     argmax canvas equals the previous step's; it stops when that count
-    reaches k and its mean entropy is at most c (exact rational comparison).
+    reaches k and its mean entropy is at most c (exact rational comparison);
+    a row holding a non-finite entropy is not confident.
 """
 from fractions import Fraction
 
@@ -89,9 +90,12 @@ class StableConfidentStopping:
         for b in range(B):
             same = self.prev is not None and bool(np.array_equal(argmax[b], self.prev[b]))
             self.count[b] = self.count[b] + 1 if same else 0
-            total = sum((Fraction(float(h)) for h in np.asarray(entropy, dtype=np.float32)[b]),
-                        Fraction(0))
-            confident = total <= Fraction(self.c) * L
+            hs = np.asarray(entropy, dtype=np.float32)[b]
+            if not np.isfinite(hs).all():
+                confident = False                  # a non-finite entropy is never confident
+            else:
+                total = sum((Fraction(float(h)) for h in hs), Fraction(0))
+                confident = total <= Fraction(self.c) * L
             done[b] = self.count[b] >= self.k and confident
         self.prev = argmax.copy()
         return done

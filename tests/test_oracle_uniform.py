@@ -102,6 +102,8 @@ def test_stable_confident_stopping_counts_and_exact_mean():
     assert stop(b, h2).tolist() == [False, True]          # a hair above the mean bound
     zero = oracle.StableConfidentStopping(0, 0.1)
     assert zero(a, np.zeros((2, 2), np.float32)).tolist() == [True, True]
+    h3 = np.array([[np.inf, 0.0], [np.nan, 0.0]], np.float32)
+    assert zero(a, h3).tolist() == [False, False]         # non-finite: never confident
 
 
 def test_uniform_loop_converges_to_the_models_canvas_and_freezes_rows():
