@@ -19,7 +19,8 @@ import torch
 __all__ = ["Stats", "Rule", "token_stats", "threshold_transfer", "topk_transfer",
            "factor_transfer", "entropy_bound_transfer", "edit_transfer",
            "transfer_schedule", "block_ranges", "block_causal_mask",
-           "workspace_size", "library_path", "load_library", "commit_step", "CommitStep"]
+           "workspace_size", "library_path", "load_library", "commit_step", "CommitStep",
+           "linear_temperature", "uniform_canvas", "renoise", "StableConfidentStopping"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libdllm_commit.so")
@@ -31,7 +32,7 @@ _SCORES = {"prob": SCORE_PROB, "margin": SCORE_MARGIN, "neg_entropy": SCORE_NEG_
 MAX_L = 4096
 MAX_SUPPRESS = 64
 
-Stats = namedtuple("Stats", ["x0", "prob", "entropy", "margin"])
+Stats = namedtuple("Stats", ["x0", "prob", "entropy", "margin", "argmax"])
 CommitStep = namedtuple("CommitStep", ["stats", "counts"])
 
 
@@ -39,6 +40,11 @@ class _CRule(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int), ("mask", ctypes.c_void_p), ("out", ctypes.c_void_p),
                 ("param", ctypes.c_double), ("strict", ctypes.c_int),
                 ("k", ctypes.c_void_p), ("tokens", ctypes.c_void_p), ("score", ctypes.c_int)]
+
+
+class _CStatsExtra(ctypes.Structure):
+    _fields_ = [("margin", ctypes.c_void_p), ("argmax", ctypes.c_void_p),
+                ("stats_temperature", ctypes.c_float)]
 
 
 class _CCanvas(ctypes.Structure):
@@ -66,6 +72,12 @@ _SIGNATURES = {
     "dllm_transfer_schedule": (_I32, [_P, _I64, ctypes.c_int32, _P, _P]),
     "dllm_block_ranges": (_I64, [_I64, _I64, _I64, _I32, _P, _I64]),
     "dllm_block_causal_mask": (_I32, [_I64, _I64, _P, _P]),
+    "dllm_linear_temperature": (_I32, [_I32, _I32, ctypes.c_double, ctypes.c_double,
+                                       ctypes.POINTER(ctypes.c_double)]),
+    "dllm_uniform_canvas": (_I32, [_P, _I64, _I64, _I64, ctypes.c_uint64, ctypes.c_uint64, _P]),
+    "dllm_renoise": (_I32, [_P, _P, _P, _I64, _I64, _P, _P]),
+    "dllm_stable_confident_stop": (_I32, [_P, _P, _I64, _I64, _I32, ctypes.c_double, _I32, _P, _P,
+                                          _P, _P]),
     "dllm_last_error": (ctypes.c_char_p, []),
 }
 
@@ -207,22 +219,25 @@ def _row_stride(logits):
 
 
 def token_stats(logits, temperature=0.0, seed=None, step=0, suppress_ids=(), rules=(),
-                out=None, workspace=None, margin=False):
+                out=None, workspace=None, margin=False, argmax=False, stats_temperature=None):
     """Per-position (x0, prob, entropy, margin) of (B, L, V) float32 / bfloat16 logits.
 
     temperature > 0 draws x0 by Gumbel-max and then needs an explicit ``seed``
     (an integer key; ``step`` selects the per-step noise).  ``rules`` is a list
     of up to two Rule objects run in the same launch; their ``out`` tensors
     are filled.  ``margin`` (or a rule ranking by margin) adds the topk_margin
-    confidence p1 - p2; otherwise Stats.margin is None.  ``out`` may give
+    confidence p1 - p2; otherwise Stats.margin is None.  ``argmax`` adds the
+    greedy argmax (useful when x0 is sampled).  ``stats_temperature`` Ts makes
+    prob / entropy / margin those of softmax(logits / Ts).  ``out`` may give
     preallocated (x0, prob, entropy[, margin]) tensors.
     """
     return _stats_call(logits, temperature, seed, step, suppress_ids, rules, out, workspace,
-                       None, margin)
+                       None, margin, argmax, stats_temperature)
 
 
 def commit_step(logits, tokens, rules, temperature=0.0, seed=None, step=0, suppress_ids=(),
-                skip_rows=True, counts=True, out=None, workspace=None, margin=False):
+                skip_rows=True, counts=True, out=None, workspace=None, margin=False, argmax=False,
+                stats_temperature=None):
     """One step of the decoding loop in one launch: token_stats with up to one
     ranking rule and one edit rule, then ``tokens`` (B, L) int32 is updated in
     place to x0 wherever a position was committed or edited.
@@ -250,12 +265,12 @@ def commit_step(logits, tokens, rules, temperature=0.0, seed=None, step=0, suppr
     canvas.counts = counts.data_ptr() if counts is not None else None
     canvas.skip_rows = int(bool(skip_rows))
     stats = _stats_call(logits, temperature, seed, step, suppress_ids, rules, out, workspace,
-                        (canvas, tokens, counts), margin)
+                        (canvas, tokens, counts), margin, argmax, stats_temperature)
     return CommitStep(stats, counts)
 
 
 def _stats_call(logits, temperature, seed, step, suppress_ids, rules, out, workspace, canvas,
-                margin):
+                margin, argmax=False, stats_temperature=None):
     _dev(logits, "logits")
     if logits.dim() != 3:
         raise ValueError("logits must be (B, L, V)")
@@ -282,6 +297,11 @@ def _stats_call(logits, temperature, seed, step, suppress_ids, rules, out, works
         mar = torch.empty((B, L), dtype=torch.float32, device=dev)
     if mar is not None:
         _bl(mar, "margin", (torch.float32,), (B, L))
+    am = torch.empty((B, L), dtype=torch.int32, device=dev) if argmax else None
+    extra = _CStatsExtra()
+    extra.margin = mar.data_ptr() if mar is not None else None
+    extra.argmax = am.data_ptr() if am is not None else None
+    extra.stats_temperature = float(stats_temperature) if stats_temperature else 0.0
     sup = (ctypes.c_int32 * max(len(suppress_ids), 1))(*[int(s) for s in suppress_ids])
     crules = (_CRule * 2)()
     keep = []
@@ -310,8 +330,7 @@ def _stats_call(logits, temperature, seed, step, suppress_ids, rules, out, works
         ws = workspace if workspace is not None else _workspace(dev, need)
         args = [logits.data_ptr(), dt, B, L, V, row_stride, float(temperature),
                 int(seed or 0) & 0xFFFFFFFFFFFFFFFF, int(step), sup, len(suppress_ids),
-                x0.data_ptr(), prob.data_ptr(), ent.data_ptr(),
-                mar.data_ptr() if mar is not None else None,
+                x0.data_ptr(), prob.data_ptr(), ent.data_ptr(), ctypes.byref(extra),
                 crules if len(rules) else None, len(rules)]
         if canvas is None:
             _check(lib.dllm_token_stats(*args, ws.data_ptr(), ws.numel(), _stream(logits)),
@@ -319,7 +338,7 @@ def _stats_call(logits, temperature, seed, step, suppress_ids, rules, out, works
         else:
             _check(lib.dllm_commit_step(*args, ctypes.byref(canvas[0]), ws.data_ptr(),
                                         ws.numel(), _stream(logits)), "dllm_commit_step")
-    return Stats(x0, prob, ent, mar)
+    return Stats(x0, prob, ent, mar, am)
 
 
 def _rule_out(conf, candidates, out):
@@ -427,3 +446,73 @@ def block_causal_mask(L, block_len, device="cuda", out=None):
         _check(load_library().dllm_block_causal_mask(int(L), int(block_len), out.data_ptr(),
                                                      _stream(out)), "dllm_block_causal_mask")
     return out
+
+
+# ---------------------------------------------------------------- uniform-noise decoding
+
+def linear_temperature(remaining, num_steps, t_min=0.4, t_max=0.8):
+    """t_min + (t_max - t_min) * remaining / num_steps."""
+    out = ctypes.c_double()
+    _check(load_library().dllm_linear_temperature(int(remaining), int(num_steps), float(t_min),
+                                                   float(t_max), ctypes.byref(out)),
+           "dllm_linear_temperature")
+    return out.value
+
+
+def uniform_canvas(shape, vocab_size, seed, draw, device=None, out=None):
+    """(B, L) int32 tokens uniform on [0, vocab_size) (Philox, counter-based)."""
+    B, L = shape
+    dev = torch.device(device) if device is not None else (out.device if out is not None
+                                                           else torch.device("cuda"))
+    if out is None:
+        out = torch.empty((B, L), dtype=torch.int32, device=dev)
+    _bl(out, "out", (torch.int32,), (B, L))
+    with torch.cuda.device(out.device):
+        _check(load_library().dllm_uniform_canvas(out.data_ptr(), B, L, int(vocab_size),
+                                                  int(seed) & 0xFFFFFFFFFFFFFFFF, int(draw),
+                                                  _stream(out)), "dllm_uniform_canvas")
+    return out
+
+
+def renoise(sample, accepted, noise, out=None):
+    """where(accepted, sample, noise)."""
+    _bl(sample, "sample", (torch.int32,))
+    B, L = sample.shape
+    _bl(accepted, "accepted", _MASK_DTYPES, (B, L))
+    _bl(noise, "noise", (torch.int32,), (B, L))
+    if out is None:
+        out = torch.empty_like(sample)
+    _bl(out, "out", (torch.int32,), (B, L))
+    with torch.cuda.device(sample.device):
+        _check(load_library().dllm_renoise(sample.data_ptr(), accepted.data_ptr(),
+                                           noise.data_ptr(), B, L, out.data_ptr(),
+                                           _stream(sample)), "dllm_renoise")
+    return out
+
+
+class StableConfidentStopping:
+    """Per-row stop of the uniform-noise loop: stability_threshold consecutive
+    unchanged argmax canvases and mean entropy <= confidence_threshold.  Call
+    with (argmax, entropy); returns the (B,) bool done tensor, which only
+    grows."""
+
+    def __init__(self, stability_threshold=1, confidence_threshold=0.005):
+        self.k, self.c = int(stability_threshold), float(confidence_threshold)
+        self.prev = self.count = self.done = None
+
+    def __call__(self, argmax, entropy):
+        _bl(argmax, "argmax", (torch.int32,))
+        B, L = argmax.shape
+        _bl(entropy, "entropy", (torch.float32,), (B, L))
+        first = self.prev is None
+        if first:
+            dev = argmax.device
+            self.prev = torch.empty((B, L), dtype=torch.int32, device=dev)
+            self.count = torch.zeros((B,), dtype=torch.int32, device=dev)
+            self.done = torch.zeros((B,), dtype=torch.uint8, device=dev)
+        with torch.cuda.device(argmax.device):
+            _check(load_library().dllm_stable_confident_stop(
+                argmax.data_ptr(), entropy.data_ptr(), B, L, self.k, self.c, int(first),
+                self.prev.data_ptr(), self.count.data_ptr(), self.done.data_ptr(),
+                _stream(argmax)), "dllm_stable_confident_stop")
+        return self.done.bool()

@@ -91,8 +91,8 @@ namespace {
 int stats_step(const char *who, const void *logits, int dtype, int64_t B, int64_t L, int64_t V,
                int64_t row_stride, float temperature, uint64_t seed, uint64_t step,
                const int32_t *suppress_ids, int n_suppress, int32_t *x0, float *prob,
-               float *entropy, float *margin, const dllm_rule *rules, int n_rules,
-               const dllm_canvas *canvas,
+               float *entropy, const dllm_stats_extra *extra, const dllm_rule *rules,
+               int n_rules, const dllm_canvas *canvas,
                void *workspace, size_t workspace_bytes, hipStream_t stream) {
   if (dtype != DLLM_F32 && dtype != DLLM_BF16)
     return fail(DLLM_ERR_DTYPE, "%s: dtype %d is neither DLLM_F32 nor DLLM_BF16", who, dtype);
@@ -112,6 +112,12 @@ int stats_step(const char *who, const void *logits, int dtype, int64_t B, int64_
   if (B == 0 || L == 0) return ok();
   if (!logits || !x0 || !prob || !entropy)
     return fail(DLLM_ERR_ARG, "%s: logits, x0, prob and entropy must be non-NULL", who);
+  float *margin = extra ? extra->margin : nullptr;
+  int32_t *argmax = extra ? extra->argmax : nullptr;
+  float stats_t = extra ? extra->stats_temperature : 0.0f;
+  if (stats_t == 0.0f) stats_t = 1.0f;
+  if (!(stats_t > 0.0f) || stats_t == __builtin_inff())
+    return fail(DLLM_ERR_ARG, "%s: stats_temperature must be 0 (none) or finite and > 0", who);
 
   StatsArgs a;
   memset(&a, 0, sizeof(a));
@@ -142,7 +148,7 @@ int stats_step(const char *who, const void *logits, int dtype, int64_t B, int64_
     seen[r.kind] = true;
     outs[i] = r.out;
     if (r.out == (const void *)x0 || r.out == (const void *)prob || r.out == (const void *)entropy ||
-        (margin && r.out == (const void *)margin) ||
+        (margin && r.out == (const void *)margin) || (argmax && r.out == (const void *)argmax) ||
         r.out == (const void *)r.mask || r.out == (const void *)logits)
       return fail(DLLM_ERR_ARG, "%s: rules[%d].out aliases another array", who, i);
     if (r.kind == DLLM_RULE_EDIT) {
@@ -173,7 +179,7 @@ int stats_step(const char *who, const void *logits, int dtype, int64_t B, int64_
   if (canvas) {
     if (a.n_rank_rules > 1)
       return fail(DLLM_ERR_ARG, "%s: a canvas step takes at most one ranking rule", who);
-    const void *arrays[] = {logits, x0, prob, entropy, margin, outs[0], outs[1]};
+    const void *arrays[] = {logits, x0, prob, entropy, margin, argmax, outs[0], outs[1]};
     for (const void *q : arrays)
       if (q && (q == (const void *)canvas->tokens || q == (const void *)canvas->counts))
         return fail(DLLM_ERR_ARG, "%s: canvas tokens or counts alias another array", who);
@@ -221,7 +227,8 @@ int stats_step(const char *who, const void *logits, int dtype, int64_t B, int64_
   a.prob = prob;
   a.entropy = entropy;
   a.margin = margin;
-
+  a.argmax = argmax;
+  a.c2 = (float)(1.4426950408889634 / (double)stats_t);
   const bool sample = temperature > 0.0f;
   size_t smem = a.n_rank_rules ? rule_smem_bytes((int)L, p.nt) : 0;
   if (p.slices > 1) smem = std::max(smem, (size_t)p.slices * sizeof(Partial));
@@ -239,22 +246,24 @@ int stats_step(const char *who, const void *logits, int dtype, int64_t B, int64_
 extern "C" int dllm_token_stats(const void *logits, int dtype, int64_t B, int64_t L, int64_t V,
                                 int64_t row_stride, float temperature, uint64_t seed,
                                 uint64_t step, const int32_t *suppress_ids, int n_suppress,
-                                int32_t *x0, float *prob, float *entropy, float *margin,
-                                const dllm_rule *rules, int n_rules, void *workspace,
-                                size_t workspace_bytes, hipStream_t stream) {
+                                int32_t *x0, float *prob, float *entropy,
+                                const dllm_stats_extra *extra, const dllm_rule *rules,
+                                int n_rules, void *workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
   return stats_step("dllm_token_stats", logits, dtype, B, L, V, row_stride, temperature, seed,
-                    step, suppress_ids, n_suppress, x0, prob, entropy, margin, rules, n_rules,
+                    step, suppress_ids, n_suppress, x0, prob, entropy, extra, rules, n_rules,
                     nullptr, workspace, workspace_bytes, stream);
 }
 
 extern "C" int dllm_commit_step(const void *logits, int dtype, int64_t B, int64_t L, int64_t V,
                                 int64_t row_stride, float temperature, uint64_t seed,
                                 uint64_t step, const int32_t *suppress_ids, int n_suppress,
-                                int32_t *x0, float *prob, float *entropy, float *margin,
-                                const dllm_rule *rules, int n_rules, const dllm_canvas *canvas,
-                                void *workspace, size_t workspace_bytes, hipStream_t stream) {
+                                int32_t *x0, float *prob, float *entropy,
+                                const dllm_stats_extra *extra, const dllm_rule *rules,
+                                int n_rules, const dllm_canvas *canvas, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
   if (!canvas) return fail(DLLM_ERR_ARG, "dllm_commit_step: canvas is NULL");
   return stats_step("dllm_commit_step", logits, dtype, B, L, V, row_stride, temperature, seed,
-                    step, suppress_ids, n_suppress, x0, prob, entropy, margin, rules, n_rules,
+                    step, suppress_ids, n_suppress, x0, prob, entropy, extra, rules, n_rules,
                     canvas, workspace, workspace_bytes, stream);
 }

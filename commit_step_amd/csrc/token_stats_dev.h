@@ -120,6 +120,8 @@ struct StatsArgs {
   float *prob;
   float *entropy;
   float *margin;           // or NULL
+  int32_t *argmax;         // greedy first argmax (also when sampling), or NULL
+  float c2;                // log2 e / Ts: Ts the statistics temperature
   const uint8_t *edit_mask;
   uint8_t *edit_out;
   const int32_t *edit_tokens;
@@ -169,6 +171,7 @@ template <> struct ElemT<float> {
 // weights relative to M itself (2^((x - M) log2 e)) when the stream ends,
 // using the exact residual M log2e - R.
 struct WaveState {
+  float c;       // log2 e / Ts: exponents are x c - R (Ts the statistics temperature)
   float M;       // wave-uniform running max
   float R;       // wave-uniform reference RN(M log2 e)
   int idx;       // wave-uniform first index of M
@@ -234,14 +237,14 @@ __device__ __forceinline__ void chunk_update(WaveState &st, const float (&x)[U *
     // ties and re-enter through zx).  Counting and locating them runs on the
     // scalar unit from ballots.
     const float cmw = wave_max(cm);
-    const float Rn = cmw * kLog2e;
+    const float Rn = cmw * st.c;
     if (RUNNER_UP) st.m2x = fmaxf(st.m2x, st.M);   // the old maximum is now a runner-up
     if (st.M != -kInf) {
       const float delta = st.R - Rn;
       const float f = __builtin_amdgcn_exp2f(delta);
       st.S = f * fmaf(delta, st.z, st.S);
       st.z = st.z * f;
-      const float e0 = fmaf(st.M, kLog2e, -st.R);      // exact residual
+      const float e0 = fmaf(st.M, st.c, -st.R);        // exact residual
       const float w0 = __builtin_amdgcn_exp2f(e0);
       const float zx1 = st.zx + w0;
       st.Sx = f * fmaf(delta, zx1, fmaf(w0, e0, st.Sx));
@@ -262,7 +265,7 @@ __device__ __forceinline__ void chunk_update(WaveState &st, const float (&x)[U *
         m[j] = __builtin_amdgcn_ballot_w64(eq);
         cnt += __builtin_popcountll(m[j]);
         lanes |= m[j];
-        const float d = clamp_d(fmaf(xv, kLog2e, -Rn));
+        const float d = clamp_d(fmaf(xv, st.c, -Rn));
         const float t = eq ? 0.0f : __builtin_amdgcn_exp2f(d);
         st.z += t;
         st.S = fmaf(t, d, st.S);
@@ -284,7 +287,7 @@ __device__ __forceinline__ void chunk_update(WaveState &st, const float (&x)[U *
     }
     if (cnt > 1) {
       // ties of the new maximum weigh 2^e1 against R
-      const float e1 = fmaf(cmw, kLog2e, -Rn);
+      const float e1 = fmaf(cmw, st.c, -Rn);
       const float w1 = (float)(cnt - 1) * __builtin_amdgcn_exp2f(e1);
       st.zx += w1;
       st.Sx = fmaf(w1, e1, st.Sx);
@@ -294,7 +297,7 @@ __device__ __forceinline__ void chunk_update(WaveState &st, const float (&x)[U *
     const float nR = -st.R;
 #pragma unroll
     for (int e = 0; e < CH; ++e) {
-      const float d = clamp_d(fmaf(x[e], kLog2e, nR));
+      const float d = clamp_d(fmaf(x[e], st.c, nR));
       const float t = __builtin_amdgcn_exp2f(d);
       st.z += t;
       st.S = fmaf(t, d, st.S);
@@ -312,14 +315,14 @@ __device__ __forceinline__ void chunk_update(WaveState &st, const float (&x)[U *
 __device__ __forceinline__ void to_max_relative(const WaveState &st, float &z, float &S) {
   if (st.M == -kInf) return;
   if (!bits_finite(__float_as_uint(st.R))) { z = __builtin_nanf(""); return; }
-  const float e = fmaf(st.M, kLog2e, -st.R);
+  const float e = fmaf(st.M, st.c, -st.R);
   const float g = __builtin_amdgcn_exp2f(-e);
   S = g * fmaf(-e, z, S);
   z = g * z;
 }
 
 // Merge partial b into a (a, b relative to their own maxima).
-__device__ __forceinline__ void merge_partial(Partial &a, const Partial &b) {
+__device__ __forceinline__ void merge_partial(Partial &a, const Partial &b, float c) {
   if (b.M == -kInf) return;
   if (a.M == -kInf) {
     const float sb = a.sb; const int ib = a.ib; const float xb = a.xb;
@@ -329,7 +332,7 @@ __device__ __forceinline__ void merge_partial(Partial &a, const Partial &b) {
   } else {
     Partial w = a, o = b;
     if (b.M > a.M || (b.M == a.M && b.idx < a.idx)) { w = b; o = a; }
-    const float delta = (o.M - w.M) * kLog2e;
+    const float delta = (o.M - w.M) * c;
     const float f = __builtin_amdgcn_exp2f(delta);
     const float zo = 1.0f + o.z;
     const float z = w.z + zo * f;
@@ -376,6 +379,7 @@ __device__ void stream_slice(const StatsArgs &a, const T *row, int64_t lo, int64
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   WaveState st;
+  st.c = a.c2;
   st.M = -kInf; st.R = -kInf; st.idx = kIdxNone; st.zx = 0.f; st.Sx = 0.f; st.z = 0.f; st.S = 0.f;
   st.sb = -kInf; st.ib = kIdxNone; st.xb = -kInf; st.m2 = -kInf; st.m2x = -kInf;
   // Greedy rows sweep their full iterations starting at a row-dependent one
@@ -534,14 +538,14 @@ __device__ void stream_slice(const StatsArgs &a, const T *row, int64_t lo, int64
   if (tid == 0) {
     Partial acc = wave_parts[0];
     for (int w = 1; w < NT / 64; ++w) {
-      merge_partial(acc, wave_parts[w]);
+      merge_partial(acc, wave_parts[w], a.c2);
       if constexpr (SAMPLE) merge_sample(acc, wave_parts[w]);
     }
     *out = acc;
   }
 }
 
-struct RowResult { int x0; float prob; float ent; float margin; };
+struct RowResult { int x0; float prob; float ent; float margin; int argmax; };
 
 // Plain two-pass recomputation of a degenerate row (NaN, +inf, or no finite
 // unsuppressed logit), with the limit semantics of the header.  Every thread
@@ -592,7 +596,7 @@ __device__ RowResult slow_row(const StatsArgs &a, const T *row, uint32_t b, uint
     if (finite) {
       if (v != s_im) {
         r2 = fmaxf(r2, x);
-        const float d = (x - M) * kLog2e;
+        const float d = (x - M) * a.c2;
         const float t = __builtin_amdgcn_exp2f(d);
         z += t;
         if (t > 0.f) S = fmaf(t, d, S);
@@ -617,7 +621,7 @@ __device__ RowResult slow_row(const StatsArgs &a, const T *row, uint32_t b, uint
   rs[tid] = r2;
   __syncthreads();
   RowResult r;
-  r.x0 = 0; r.prob = 0.f; r.ent = 0.f; r.margin = 0.f;
+  r.x0 = 0; r.prob = 0.f; r.ent = 0.f; r.margin = 0.f; r.argmax = 0;
   if (tid == 0) {
     float Z = 0.f, SS = 0.f, SB = -kInf, XB = -kInf, R2 = -kInf; int IB = kIdxNone;
     for (int t = 0; t < NT; ++t) {
@@ -629,21 +633,24 @@ __device__ RowResult slow_row(const StatsArgs &a, const T *row, uint32_t b, uint
     }
     if (finite) {
       r.ent = log1pf(Z) - kLn2 * SS / (1.0f + Z);
-      r.margin = -expm1f(R2 - M) / (1.0f + Z);
+      r.margin = -expm1f((R2 - M) * a.c2 * kLn2) / (1.0f + Z);
+      r.argmax = s_im;
       if (SAMPLE) {
         r.x0 = IB;
-        r.prob = __builtin_amdgcn_exp2f((XB - M) * kLog2e) / (1.0f + Z);
+        r.prob = __builtin_amdgcn_exp2f((XB - M) * a.c2) / (1.0f + Z);
       } else {
         r.x0 = s_im;
         r.prob = 1.0f / (1.0f + Z);
       }
     } else if (M == -kInf) {
       r.x0 = SAMPLE ? IB : a.first_allowed;
+      r.argmax = a.first_allowed;
       r.prob = 1.0f / (float)nA;
       r.ent = logf((float)nA);
       r.margin = nA == 1 ? 1.0f : 0.0f;
     } else {
       r.x0 = SAMPLE ? IB : s_iinf;
+      r.argmax = s_iinf;
       r.prob = 1.0f / (float)s_ninf;
       r.ent = logf((float)s_ninf);
       r.margin = s_ninf == 1 ? 1.0f : 0.0f;
@@ -663,17 +670,18 @@ __device__ __forceinline__ bool row_needed(const StatsArgs &a, int64_t row_id) {
 // degenerate (NaN, +inf, or no finite unsuppressed logit) and needs the
 // two-pass path.
 template <bool SAMPLE>
-__device__ __forceinline__ bool finalize_partial(const Partial &p, RowResult &res) {
+__device__ __forceinline__ bool finalize_partial(const Partial &p, float c, RowResult &res) {
   const bool ok = bits_finite(__float_as_uint(p.M)) && bits_finite(__float_as_uint(p.z)) &&
                   bits_finite(__float_as_uint(p.S)) &&
                   (!SAMPLE || (p.ib != kIdxNone && bits_finite(__float_as_uint(p.sb))));
   if (ok) {
     const float zf = 1.0f + p.z;
     res.ent = log1pf(p.z) - kLn2 * p.S / zf;
-    res.margin = -expm1f(p.R2 - p.M) / zf;          // (1 - e^(runner-up - max)) / z
+    res.margin = -expm1f((p.R2 - p.M) * c * kLn2) / zf;   // (1 - e^((runner-up - max)/Ts)) / z
+    res.argmax = p.idx;
     if (SAMPLE) {
       res.x0 = p.ib;
-      res.prob = __builtin_amdgcn_exp2f((p.xb - p.M) * kLog2e) / zf;
+      res.prob = __builtin_amdgcn_exp2f((p.xb - p.M) * c) / zf;
     } else {
       res.x0 = p.idx;
       res.prob = 1.0f / zf;
@@ -690,6 +698,7 @@ __device__ __forceinline__ int publish_row(const StatsArgs &a, int64_t row_id,
   store_coherent(&a.prob[row_id], res.prob);
   store_coherent(&a.entropy[row_id], res.ent);
   if (a.margin) store_coherent(&a.margin[row_id], res.margin);
+  if (a.argmax) a.argmax[row_id] = res.argmax;
   if (!a.has_edit) return 0;
   const uint8_t e = edit_decision(a.edit_mask[row_id], res.x0, a.edit_tokens[row_id],
                                   res.prob, a.edit_tau);
@@ -819,7 +828,7 @@ __global__ __launch_bounds__(NT) void token_stats_kernel(StatsArgs a) {
     if (tid == 0) {
       Partial acc = lds[0];
       for (int s = 1; s < a.slices; ++s) {       // fixed slice order: reproducible
-        merge_partial(acc, lds[s]);
+        merge_partial(acc, lds[s], a.c2);
         if (SAMPLE) merge_sample(acc, lds[s]);
       }
       slice_parts_acc = acc;
@@ -831,8 +840,8 @@ __global__ __launch_bounds__(NT) void token_stats_kernel(StatsArgs a) {
   // Finalize the row.
   __shared__ int s_slow;
   RowResult res;
-  res.x0 = 0; res.prob = 0.f; res.ent = 0.f; res.margin = 0.f;
-  if (tid == 0) s_slow = !finalize_partial<SAMPLE>(slice_parts_acc, res);
+  res.x0 = 0; res.prob = 0.f; res.ent = 0.f; res.margin = 0.f; res.argmax = 0;
+  if (tid == 0) s_slow = !finalize_partial<SAMPLE>(slice_parts_acc, a.c2, res);
   __syncthreads();
   if (s_slow) res = slow_row<T, NT, SAMPLE>(a, row, b, l, slow_scratch);
   if (tid == 0 && publish_row(a, row_id, res) && a.counts) atomicAdd(&a.edit_count[b], 1u);

@@ -104,6 +104,29 @@ typedef struct {
   int score;
 } dllm_rule;
 
+/* Optional outputs and options of dllm_token_stats / dllm_commit_step.
+ *   margin   (B, L) float32 DEVICE output, or NULL: p_(1) - p_(2) of the
+ *            softmax over the unsuppressed ids, the topk_margin confidence
+ *            (mojo-dllm "The GPU path": p minus the runner-up's probability,
+ *            the runner-up being the largest logit at any index but the first
+ *            maximal one; a tie gives 0, one unsuppressed id gives 1), whatever
+ *            x0 is.
+ *   argmax   (B, L) int32 DEVICE output, or NULL: the first index of the
+ *            largest logit, also when x0 is sampled (the DiffusionGemma loop of
+ *            mlx-arsenal "Uniform-noise decoding (DiffusionGemma)" keeps both
+ *            the argmax canvas and a categorical sample).
+ *   stats_temperature  0 (none) or Ts > 0, finite: prob, entropy and margin
+ *            are those of softmax(logits / Ts) (that loop measures entropy on
+ *            the temperature-scaled logits); x0 and argmax do not depend on
+ *            it.  With temperature = Ts too, x0 is a categorical sample of
+ *            softmax(logits / Ts).
+ * Zero-fill the struct before setting its fields. */
+typedef struct {
+  float *margin;
+  int32_t *argmax;
+  float stats_temperature;
+} dllm_stats_extra;
+
 /* ---------------------------------------------------------------------------
  * dllm_token_stats -- per position: the proposed token x0, its probability and
  * the entropy of the position's distribution (mlx-arsenal "dLLM block
@@ -128,11 +151,8 @@ typedef struct {
  *   prob         (B, L) float32 DEVICE output: softmax(logits)[x0], untempered.
  *   entropy      (B, L) float32 DEVICE output: -sum p log p of softmax(logits)
  *                over the unsuppressed ids (natural log), untempered.
- *   margin       (B, L) float32 DEVICE output, or NULL: p_(1) - p_(2) of
- *                softmax(logits) over the unsuppressed ids, the topk_margin
- *                confidence (the runner-up is the largest logit at any index
- *                but the first maximal one; a tie gives 0, one unsuppressed id
- *                gives 1), untempered, whatever x0 is.
+ *   extra        HOST struct of optional outputs and options, or NULL (all
+ *                off): see dllm_stats_extra.
  *   rules        HOST array of n_rules (0..2) rules fused into the same launch,
  *                or NULL.  At most one rule of each kind.
  *   workspace    DEVICE scratch of at least dllm_token_stats_workspace_size()
@@ -150,7 +170,7 @@ int dllm_token_stats(const void *logits, int dtype, int64_t B, int64_t L,
                      uint64_t seed, uint64_t step,
                      const int32_t *suppress_ids, int n_suppress,
                      int32_t *x0, float *prob, float *entropy,
-                     float *margin,
+                     const dllm_stats_extra *extra,
                      const dllm_rule *rules, int n_rules,
                      void *workspace, size_t workspace_bytes,
                      hipStream_t stream);
@@ -203,7 +223,7 @@ int dllm_commit_step(const void *logits, int dtype, int64_t B, int64_t L,
                      uint64_t seed, uint64_t step,
                      const int32_t *suppress_ids, int n_suppress,
                      int32_t *x0, float *prob, float *entropy,
-                     float *margin,
+                     const dllm_stats_extra *extra,
                      const dllm_rule *rules, int n_rules,
                      const dllm_canvas *canvas,
                      void *workspace, size_t workspace_bytes,
@@ -276,6 +296,54 @@ int64_t dllm_block_ranges(int64_t prompt_len, int64_t gen_len,
  * k / block_len <= q / block_len, else -inf.  out (L, L) float32 DEVICE. */
 int dllm_block_causal_mask(int64_t L, int64_t block_len, float *out,
                            hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Uniform-noise decoding (mlx-arsenal "dLLM block decoding", function table
+ * row linear_temperature / uniform_canvas / renoise / StableConfidentStopping,
+ * and the loop of "Uniform-noise decoding (DiffusionGemma)"; mlxcel "Block
+ * Diffusion", "DiffusionGemma Canvas Denoising").  One step of that loop is a
+ * dllm_token_stats launch with temperature = stats_temperature = T (x0 the
+ * categorical sample, extra->argmax the argmax canvas, entropy of the scaled
+ * logits) and a fused entropy_bound rule over every position, then
+ * dllm_uniform_canvas + dllm_renoise for the new canvas and
+ * dllm_stable_confident_stop for the per-row stop.
+ * -------------------------------------------------------------------------*/
+
+/* linear_temperature: *out = t_min + (t_max - t_min) * remaining / num_steps
+ * (the temperature falls linearly with the remaining steps: t_max when
+ * remaining = num_steps).  0 <= remaining <= num_steps, num_steps >= 1.
+ * Host only. */
+int dllm_linear_temperature(int remaining, int num_steps, double t_min,
+                            double t_max, double *out);
+
+/* uniform_canvas: out[b, l] uniform on [0, V): with w the four words of
+ * Philox4x32-10 (key = seed low 32, seed high 32) at counter
+ * (l, b, 0xFFFFFFFF, draw) and x = w0 + 2^32 w1, out = floor(x V / 2^64)
+ * (bias at most V / 2^64).  draw < 2^32 picks an independent canvas (the
+ * sampling noise of dllm_token_stats never uses counter word 2 = 0xFFFFFFFF).
+ * out (B, L) int32 DEVICE; V in [1, 2^31). */
+int dllm_uniform_canvas(int32_t *out, int64_t B, int64_t L, int64_t V,
+                        uint64_t seed, uint64_t draw, hipStream_t stream);
+
+/* renoise: out = where(accepted, sample, noise).  sample, noise, out (B, L)
+ * int32 DEVICE (out may be sample or noise); accepted (B, L) uint8. */
+int dllm_renoise(const int32_t *sample, const uint8_t *accepted,
+                 const int32_t *noise, int64_t B, int64_t L, int32_t *out,
+                 hipStream_t stream);
+
+/* StableConfidentStopping: per batch row, stable_steps[b] counts the
+ * consecutive calls whose argmax row equals the previous call's (0 on the
+ * first call, first != 0); the row is confident when the mean of its L
+ * entropies is at most confidence_threshold (exact: sum <= c L, no rounding;
+ * a non-finite entropy is never confident); done[b] |= (stable_steps[b] >=
+ * stability_threshold && confident).  prev_argmax (B, L) int32 and
+ * stable_steps (B,) int32 are the caller's state, updated in place; done (B,)
+ * uint8 in/out.  stability_threshold >= 0, confidence_threshold not NaN. */
+int dllm_stable_confident_stop(const int32_t *argmax, const float *entropy,
+                               int64_t B, int64_t L, int stability_threshold,
+                               double confidence_threshold, int first,
+                               int32_t *prev_argmax, int32_t *stable_steps,
+                               uint8_t *done, hipStream_t stream);
 
 /* Message describing the last error returned on the calling thread ("" if
  * none). */

@@ -139,6 +139,32 @@ def test_commit_step_argument_errors(lib):
     assert call(ctypes.byref(cv), B=0) == 0
 
 
+def test_uniform_helpers_argument_errors(lib):
+    import commit_step_amd as dc
+    P = ctypes.c_void_p
+    out = ctypes.c_double()
+    assert lib.dllm_linear_temperature(3, 4, 0.4, 0.8, ctypes.byref(out)) == 0
+    assert out.value == pytest.approx(0.4 + 0.4 * 3 / 4, rel=1e-15)
+    assert dc.linear_temperature(48, 48) == 0.8
+    assert lib.dllm_linear_temperature(5, 4, 0.4, 0.8, ctypes.byref(out)) == -1
+    assert lib.dllm_linear_temperature(0, 0, 0.4, 0.8, ctypes.byref(out)) == -1
+    assert lib.dllm_linear_temperature(1, 4, math.nan, 0.8, ctypes.byref(out)) == -1
+    assert lib.dllm_linear_temperature(1, 4, 0.4, 0.8, None) == -1
+    fake = P(16)
+    assert lib.dllm_uniform_canvas(fake, 1, 4, 0, 1, 0, None) == -1 and "V" in _err(lib)
+    assert lib.dllm_uniform_canvas(fake, 1, 4, 1 << 31, 1, 0, None) == -1
+    assert lib.dllm_uniform_canvas(fake, 1, 4, 10, 1, 1 << 32, None) == -1 and "draw" in _err(lib)
+    assert lib.dllm_uniform_canvas(None, 1, 4, 10, 1, 0, None) == -1
+    assert lib.dllm_uniform_canvas(None, 0, 4, 10, 1, 0, None) == 0
+    assert lib.dllm_renoise(fake, P(32), None, 2, 3, P(48), None) == -1
+    assert lib.dllm_renoise(fake, P(32), P(40), 2, 3, P(32), None) == -1 and "alias" in _err(lib)
+    stop = lib.dllm_stable_confident_stop
+    assert stop(fake, P(24), 2, 3, -1, 0.1, 1, P(32), P(40), P(48), None) == -1
+    assert stop(fake, P(24), 2, 3, 1, math.nan, 1, P(32), P(40), P(48), None) == -1
+    assert stop(fake, P(24), 2, 3, 1, 0.1, 1, fake, P(40), P(48), None) == -1 and "alias" in _err(lib)
+    assert stop(fake, P(24), 0, 3, 1, 0.1, 1, P(32), P(40), P(48), None) == 0
+
+
 def test_transfer_argument_errors(lib):
     fake = ctypes.c_void_p(16)
     assert lib.dllm_transfer_threshold(fake, fake, 1, 4, math.nan, 0, ctypes.c_void_p(32), None) == -1
