@@ -28,7 +28,7 @@ from .philox import philox4x32_10, philox_words, uniform_from_word, gumbel_noise
 from .stats import token_stats, token_stats_row, widen_logits, Stats
 from .rules import (threshold_transfer, topk_transfer, factor_transfer,
                     entropy_bound_transfer, edit_transfer, transfer_schedule,
-                    block_ranges, block_causal_mask)
+                    block_ranges, block_causal_mask, decaying_threshold)
 from .step import commit_step, apply_step, counts, rank_rule, StepResult
 from .uniform import (linear_temperature, uniform_canvas, renoise, StableConfidentStopping,
                       decode_uniform)
@@ -38,7 +38,7 @@ __all__ = [
     "token_stats", "token_stats_row", "widen_logits", "Stats",
     "threshold_transfer", "topk_transfer", "factor_transfer",
     "entropy_bound_transfer", "edit_transfer", "transfer_schedule",
-    "block_ranges", "block_causal_mask",
+    "block_ranges", "block_causal_mask", "decaying_threshold",
     "commit_step", "apply_step", "counts", "rank_rule", "StepResult",
     "linear_temperature", "uniform_canvas", "renoise", "StableConfidentStopping",
     "decode_uniform",

@@ -69,13 +69,22 @@ def threshold_transfer(conf, cand, tau, strict=False):
     commit exactly one: the first candidate of maximal confidence.
 
     Function table, threshold_transfer row; "Deviations": the forced token is the
-    first maximal one and exactly one is forced.
+    first maximal one and exactly one is forced.  tau is one threshold, or a
+    (B,) array of thresholds, one per batch row (the per-row threshold
+    schedules of mlxcel "Block Diffusion", "LLaDA-2 Block Unmasking").
     """
     conf, cand = _f32(conf, "conf"), _mask(cand, "cand")
-    tau = _check_param(tau, "tau")
     B, L = conf.shape
+    taus = np.asarray(tau, dtype=np.float64)
+    if taus.ndim == 0:
+        taus = np.full(B, float(taus))
+    if taus.shape != (B,):
+        raise ValueError("tau must be a number or a (B,) array")
+    for t in taus:
+        _check_param(float(t), "tau")
     out = np.zeros((B, L), dtype=bool)
     for b in range(B):
+        tau = float(taus[b])
         C = [l for l in range(L) if cand[b, l]]
         if not C:
             continue
@@ -88,6 +97,16 @@ def threshold_transfer(conf, cand, tau, strict=False):
             first = next(l for l in C if _conf(conf[b, l]) == best)
             out[b, first] = True
     return out
+
+
+def decaying_threshold(tau_initial, tau_floor, decay, step):
+    """max(tau_floor, tau_initial - decay * step): a threshold that falls
+    linearly with the step and stops at its floor (mlxcel "Block Diffusion",
+    "LLaDA-2 Block Unmasking": an initial / floor confidence threshold, 0.95 by
+    default, and a linearly decaying threshold)."""
+    if step < 0:
+        raise ValueError("step must be >= 0")
+    return max(float(tau_floor), float(tau_initial) - float(decay) * int(step))
 
 
 def topk_transfer(conf, cand, k):

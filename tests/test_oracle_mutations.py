@@ -71,6 +71,10 @@ MUTATIONS = [
      "c[b, 1] = 0", "hand_worked or editing_loop"),
     ("step.py", "em = edit_transfer(st.x0, prob32, tokens, editable, tau_edit)",
      "em = edit_transfer(st.x0, prob32, tokens, editable | cand, tau_edit)", "editing_loop"),
+    ("rules.py", "float(tau_initial) - float(decay) * int(step))",
+     "float(tau_initial) - float(decay) * (int(step) + 1))", "decaying"),
+    ("rules.py", "return max(float(tau_floor),", "return min(float(tau_floor),", "decaying"),
+    ("rules.py", "        tau = float(taus[b])\n", "        tau = float(taus[0])\n", "per_row"),
 ]
 
 

@@ -526,3 +526,36 @@ def test_block_causal_mask_special_cases():
         keep = M[q] == 0                                         # keep-mask form
         assert keep[: (q // 16 + 1) * 16].all() and not keep[(q // 16 + 1) * 16:].any()
     assert block_causal_mask(0, 4).shape == (0, 0)
+
+
+# ----------------------------------------------------------------- threshold schedules
+# mlxcel "Block Diffusion", "LLaDA-2 Block Unmasking": an initial / floor
+# confidence threshold (0.95 by default) and a linearly decaying threshold.
+
+def test_decaying_threshold_endpoints_slope_and_floor():
+    assert oracle.decaying_threshold(0.95, 0.95, 0.0, 31) == 0.95        # the default: constant
+    assert oracle.decaying_threshold(0.95, 0.7, 0.01, 0) == 0.95
+    assert oracle.decaying_threshold(0.95, 0.7, 0.01, 10) == pytest.approx(0.85, abs=1e-15)
+    assert oracle.decaying_threshold(0.95, 0.7, 0.01, 25) == 0.7          # reaches the floor
+    assert oracle.decaying_threshold(0.95, 0.7, 0.01, 1000) == 0.7        # and stays there
+    vals = [oracle.decaying_threshold(0.9, 0.5, 0.03, s) for s in range(12)]
+    assert all(a >= b for a, b in zip(vals, vals[1:]))
+    with pytest.raises(ValueError):
+        oracle.decaying_threshold(0.9, 0.5, 0.03, -1)
+
+
+def test_per_row_thresholds_act_row_by_row():
+    rng = np.random.default_rng(41)
+    B, L = 5, 30
+    conf = rng.random((B, L)).astype(np.float32)
+    cand = rng.random((B, L)) < 0.6
+    taus = np.array([0.2, 0.5, 0.99, 0.0, 0.7])
+    for strict in (False, True):
+        got = oracle.threshold_transfer(conf, cand, taus, strict)
+        for b in range(B):
+            one = oracle.threshold_transfer(conf[b:b + 1], cand[b:b + 1], float(taus[b]), strict)
+            assert np.array_equal(got[b:b + 1], one)
+        # a row whose threshold no candidate reaches commits exactly one
+        assert got[2].sum() == (1 if cand[2].any() else 0)
+    with pytest.raises(ValueError):
+        oracle.threshold_transfer(conf, cand, np.array([0.5, np.nan, 0.5, 0.5, 0.5]))
