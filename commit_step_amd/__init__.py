@@ -20,7 +20,8 @@ __all__ = ["Stats", "Rule", "token_stats", "threshold_transfer", "topk_transfer"
            "factor_transfer", "entropy_bound_transfer", "edit_transfer",
            "transfer_schedule", "block_ranges", "block_causal_mask",
            "workspace_size", "library_path", "load_library", "commit_step", "CommitStep",
-           "linear_temperature", "uniform_canvas", "renoise", "StableConfidentStopping"]
+           "linear_temperature", "uniform_canvas", "renoise", "StableConfidentStopping",
+           "decaying_threshold"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libdllm_commit.so")
@@ -39,7 +40,8 @@ CommitStep = namedtuple("CommitStep", ["stats", "counts"])
 class _CRule(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int), ("mask", ctypes.c_void_p), ("out", ctypes.c_void_p),
                 ("param", ctypes.c_double), ("strict", ctypes.c_int),
-                ("k", ctypes.c_void_p), ("tokens", ctypes.c_void_p), ("score", ctypes.c_int)]
+                ("k", ctypes.c_void_p), ("tokens", ctypes.c_void_p), ("score", ctypes.c_int),
+                ("taus", ctypes.c_void_p)]
 
 
 class _CStatsExtra(ctypes.Structure):
@@ -65,6 +67,9 @@ _SIGNATURES = {
                                 ctypes.c_uint64, _P, _I32, _P, _P, _P, _P, _P, _I32, _P, _P,
                                 ctypes.c_size_t, _P]),
     "dllm_transfer_threshold": (_I32, [_P, _P, _I64, _I64, ctypes.c_double, _I32, _P, _P]),
+    "dllm_transfer_threshold_rows": (_I32, [_P, _P, _P, _I64, _I64, _I32, _P, _P]),
+    "dllm_decaying_threshold": (_I32, [ctypes.c_double, ctypes.c_double, ctypes.c_double, _I64,
+                                       ctypes.POINTER(ctypes.c_double)]),
     "dllm_transfer_topk": (_I32, [_P, _P, _P, _I64, _I64, _P, _P]),
     "dllm_transfer_factor": (_I32, [_P, _P, _I64, _I64, ctypes.c_double, _P, _P]),
     "dllm_transfer_entropy_bound": (_I32, [_P, _P, _I64, _I64, ctypes.c_double, _P, _P]),
@@ -162,13 +167,18 @@ class Rule:
                  score="prob"):
         if score not in _SCORES:
             raise ValueError(f"score must be one of {sorted(_SCORES)}")
-        self.kind, self.mask, self.param, self.strict = kind, mask, float(param), bool(strict)
+        self.taus = param if isinstance(param, torch.Tensor) else None
+        if self.taus is not None and kind != RULE_THRESHOLD:
+            raise ValueError("only the threshold rule takes one threshold per row")
+        self.param = 0.0 if self.taus is not None else float(param)
+        self.kind, self.mask, self.strict = kind, mask, bool(strict)
         self.k, self.tokens, self.out, self.score = k, tokens, out, _SCORES[score]
 
     @classmethod
     def threshold(cls, candidates, tau, strict=False, score="prob"):
         """score: "prob" (LLaDA, maskgit_plus), "margin" (topk_margin) or
-        "neg_entropy" (Dream's entropy confidence)."""
+        "neg_entropy" (Dream's entropy confidence).  tau: a number, or a (B,)
+        float64 device tensor with one threshold per batch row."""
         return cls(RULE_THRESHOLD, candidates, tau, strict=strict, score=score)
 
     @classmethod
@@ -313,6 +323,8 @@ def _stats_call(logits, temperature, seed, step, suppress_ids, rules, out, works
         c = crules[i]
         c.kind, c.mask, c.out = r.kind, r.mask.data_ptr(), r.out.data_ptr()
         c.param, c.strict, c.score = r.param, int(r.strict), r.score
+        if r.taus is not None:
+            c.taus = _bl(r.taus, "taus", (torch.float64,), (B,)).data_ptr()
         if r.kind == RULE_TOPK:
             kt = _k_tensor(r.k, B, dev)
             keep.append(kt)
@@ -350,15 +362,33 @@ def _rule_out(conf, candidates, out):
 
 
 def threshold_transfer(prob, candidates, threshold, strict=False, out=None):
-    """Commit candidates with prob >= threshold (> when strict); force one if none pass."""
+    """Commit candidates with prob >= threshold (> when strict); force one if none pass.
+    threshold: a number, or a (B,) float64 device tensor, one per batch row."""
     _bl(prob, "prob", (torch.float32,))
     out = _rule_out(prob, candidates, out)
     B, L = prob.shape
+    if isinstance(threshold, torch.Tensor):
+        taus = _bl(threshold, "threshold", (torch.float64,), (B,))
+        with torch.cuda.device(prob.device):
+            _check(load_library().dllm_transfer_threshold_rows(
+                prob.data_ptr(), candidates.data_ptr(), taus.data_ptr(), B, L,
+                int(bool(strict)), out.data_ptr(), _stream(prob)), "dllm_transfer_threshold_rows")
+        return out
     with torch.cuda.device(prob.device):
         _check(load_library().dllm_transfer_threshold(
             prob.data_ptr(), candidates.data_ptr(), B, L, float(threshold), int(bool(strict)),
             out.data_ptr(), _stream(prob)), "dllm_transfer_threshold")
     return out
+
+
+def decaying_threshold(tau_initial, tau_floor, decay, step):
+    """max(tau_floor, tau_initial - decay * step): the linearly decaying
+    confidence threshold with a floor."""
+    out = ctypes.c_double()
+    _check(load_library().dllm_decaying_threshold(float(tau_initial), float(tau_floor),
+                                                   float(decay), int(step), ctypes.byref(out)),
+           "dllm_decaying_threshold")
+    return out.value
 
 
 def topk_transfer(prob, candidates, k, out=None):

@@ -37,6 +37,7 @@ struct RuleDev {
   uint8_t *out;
   const int32_t *k;
   const int32_t *tokens;
+  const double *taus;  // THRESHOLD: per-row thresholds in place of param, or null
   double param;
   // ENTROPY_BOUND, exact comparison of a finite sum with gamma: floor(gamma *
   // 2^149) as a signed fixed-point number, and 0 = use gamma_fx, 1 = always <=
@@ -487,6 +488,7 @@ __device__ inline void rule_threshold(const RuleDev &r, int b, int L, const floa
   const float *c_row = conf + (int64_t)b * L;
   const uint8_t *m_row = r.mask + (int64_t)b * L;
   uint8_t *o_row = r.out + (int64_t)b * L;
+  const double tau = r.taus ? r.taus[b] : r.param;
   int my_pass = 0;
   uint64_t my_best = kSentinel;
   for (int l = tid; l < L; l += nt) {
@@ -494,7 +496,7 @@ __device__ inline void rule_threshold(const RuleDev &r, int b, int L, const floa
     if (m_row[l]) {
       const float c = conf_sanitized(rule_conf(r, c_row + l));
       const double cd = (double)c;
-      v = (r.strict ? (cd > r.param) : (cd >= r.param)) ? 1 : 0;
+      v = (r.strict ? (cd > tau) : (cd >= tau)) ? 1 : 0;
       my_pass += v;
       const uint64_t key = ((uint64_t)conf_key(c) << 32) | (uint32_t)l;
       my_best = key < my_best ? key : my_best;

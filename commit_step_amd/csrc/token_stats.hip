@@ -149,8 +149,11 @@ int stats_step(const char *who, const void *logits, int dtype, int64_t B, int64_
     outs[i] = r.out;
     if (r.out == (const void *)x0 || r.out == (const void *)prob || r.out == (const void *)entropy ||
         (margin && r.out == (const void *)margin) || (argmax && r.out == (const void *)argmax) ||
-        r.out == (const void *)r.mask || r.out == (const void *)logits)
+        r.out == (const void *)r.mask || r.out == (const void *)logits ||
+        (r.taus && r.out == (const void *)r.taus))
       return fail(DLLM_ERR_ARG, "%s: rules[%d].out aliases another array", who, i);
+    if (r.taus && r.kind != DLLM_RULE_THRESHOLD)
+      return fail(DLLM_ERR_ARG, "%s: only the threshold rule takes per-row thresholds", who);
     if (r.kind == DLLM_RULE_EDIT) {
       const bool canvas_tokens = canvas && canvas->tokens;
       if (!r.mask || !r.out || (!r.tokens && !canvas_tokens))

@@ -90,6 +90,7 @@ int prepare_rule(const dllm_rule &r, RuleDev &d, int64_t B, int64_t L, const cha
   d.out = r.out;
   d.k = r.k;
   d.tokens = r.tokens;
+  d.taus = r.taus;
   d.param = r.param;
   d.score = r.score;
   d.negate = r.score == DLLM_SCORE_NEG_ENTROPY ? 1 : 0;
@@ -99,6 +100,10 @@ int prepare_rule(const dllm_rule &r, RuleDev &d, int64_t B, int64_t L, const cha
   if (r.score != DLLM_SCORE_PROB && r.kind != DLLM_RULE_THRESHOLD && r.kind != DLLM_RULE_TOPK &&
       r.kind != DLLM_RULE_FACTOR)
     return fail(DLLM_ERR_ARG, "%s: only threshold, topk and factor take another score", who);
+  if (r.taus && r.kind != DLLM_RULE_THRESHOLD)
+    return fail(DLLM_ERR_ARG, "%s: only the threshold rule takes per-row thresholds", who);
+  if (r.taus && (const void *)r.taus == (const void *)r.out)
+    return fail(DLLM_ERR_ARG, "%s: the output aliases the thresholds", who);
   if (r.kind == DLLM_RULE_TOPK) {
     if (!r.k) return fail(DLLM_ERR_ARG, "%s: topk needs the k array", who);
     return DLLM_OK;
@@ -214,6 +219,32 @@ extern "C" int dllm_transfer_threshold(const float *conf, const uint8_t *cand, i
   r.param = tau;
   r.strict = strict;
   return launch_batch_rule(r, B, L, conf, stream, "dllm_transfer_threshold");
+}
+
+extern "C" int dllm_transfer_threshold_rows(const float *conf, const uint8_t *cand,
+                                            const double *taus, int64_t B, int64_t L, int strict,
+                                            uint8_t *commit, hipStream_t stream) {
+  if (!taus && B > 0 && L > 0)
+    return fail(DLLM_ERR_ARG, "dllm_transfer_threshold_rows: taus must be non-NULL");
+  dllm_rule r;
+  memset(&r, 0, sizeof r);
+  r.kind = DLLM_RULE_THRESHOLD;
+  r.mask = cand;
+  r.out = commit;
+  r.taus = taus;
+  r.strict = strict;
+  return launch_batch_rule(r, B, L, conf, stream, "dllm_transfer_threshold_rows");
+}
+
+extern "C" int dllm_decaying_threshold(double tau_initial, double tau_floor, double decay,
+                                       int64_t step, double *out) {
+  if (!out) return fail(DLLM_ERR_ARG, "dllm_decaying_threshold: out must be non-NULL");
+  if (tau_initial != tau_initial || tau_floor != tau_floor || decay != decay)
+    return fail(DLLM_ERR_ARG, "dllm_decaying_threshold: an argument is NaN");
+  if (step < 0) return fail(DLLM_ERR_ARG, "dllm_decaying_threshold: step must be >= 0");
+  const double t = tau_initial - decay * (double)step;
+  *out = t > tau_floor ? t : tau_floor;
+  return DLLM_OK;
 }
 
 extern "C" int dllm_transfer_topk(const float *conf, const uint8_t *cand, const int32_t *k,

@@ -90,6 +90,11 @@ enum {
  *   tokens  EDIT only: (B, L) int32 current canvas.
  *   score   THRESHOLD / FACTOR / TOPK: DLLM_SCORE_* (0 = prob); must be 0 for
  *           the other kinds.
+ *   taus    THRESHOLD only: (B,) float64 DEVICE, one threshold per batch row
+ *           (used in place of param), or NULL.  The entries are read by the
+ *           kernel and must not be NaN (a NaN entry passes no candidate, so its
+ *           row commits only the forced one).  Per-row threshold schedules:
+ *           mlxcel "Block Diffusion", "LLaDA-2 Block Unmasking".
  * THRESHOLD / FACTOR / TOPK rank by the score (prob by default), ENTROPY_BOUND
  * by entropy, EDIT uses x0, prob and tokens.  Zero-fill the struct before
  * setting its fields. */
@@ -102,6 +107,7 @@ typedef struct {
   const int32_t *k;
   const int32_t *tokens;
   int score;
+  const double *taus;
 } dllm_rule;
 
 /* Optional outputs and options of dllm_token_stats / dllm_commit_step.
@@ -237,6 +243,23 @@ int dllm_commit_step(const void *logits, int dtype, int64_t B, int64_t L,
 int dllm_transfer_threshold(const float *conf, const uint8_t *cand, int64_t B,
                             int64_t L, double tau, int strict, uint8_t *commit,
                             hipStream_t stream);
+
+/* dllm_transfer_threshold with one threshold per batch row: taus (B,) float64
+ * DEVICE, taus[b] in place of tau for row b (mlxcel "Block Diffusion",
+ * "LLaDA-2 Block Unmasking": per-row thresholds, e.g. rows at different steps
+ * of a decaying schedule).  The entries must not be NaN (not checked: a NaN
+ * entry passes no candidate and its row commits only the forced one). */
+int dllm_transfer_threshold_rows(const float *conf, const uint8_t *cand, const double *taus,
+                                 int64_t B, int64_t L, int strict, uint8_t *commit,
+                                 hipStream_t stream);
+
+/* The linearly decaying confidence threshold (mlxcel "Block Diffusion",
+ * "LLaDA-2 Block Unmasking": an initial and a floor threshold, 0.95 by
+ * default, with an optional linear decay): *out = max(tau_floor, tau_initial -
+ * decay * step), computed in double on the host.  step >= 0; no argument may
+ * be NaN.  Returns DLLM_ERR_ARG otherwise. */
+int dllm_decaying_threshold(double tau_initial, double tau_floor, double decay, int64_t step,
+                            double *out);
 
 /* topk_transfer (topk_transfer row; mojo-dllm "The loop LLaDA uses"): commit
  * the k[b] most confident candidates of batch row b.  k (B,) int32 DEVICE;

@@ -165,6 +165,37 @@ def test_uniform_helpers_argument_errors(lib):
     assert stop(fake, P(24), 0, 3, 1, 0.1, 1, P(32), P(40), P(48), None) == 0
 
 
+def test_decaying_threshold_host_parity(lib):
+    import commit_step_amd as dc
+    for t0, fl, d in product([0.95, 0.9, 1.0, 0.5], [0.95, 0.7, 0.0, -1.0], [0.0, 0.01, 0.05, 1e-9]):
+        for s in [0, 1, 5, 31, 32, 1000, 1 << 40]:
+            assert dc.decaying_threshold(t0, fl, d, s) == oracle.decaying_threshold(t0, fl, d, s)
+    out = ctypes.c_double()
+    assert lib.dllm_decaying_threshold(0.9, 0.5, 0.1, -1, ctypes.byref(out)) == -1
+    assert lib.dllm_decaying_threshold(math.nan, 0.5, 0.1, 1, ctypes.byref(out)) == -1
+    assert lib.dllm_decaying_threshold(0.9, 0.5, math.nan, 1, ctypes.byref(out)) == -1
+    assert lib.dllm_decaying_threshold(0.9, 0.5, 0.1, 1, None) == -1
+
+
+def test_per_row_threshold_argument_errors(lib):
+    import commit_step_amd as dc
+    P = ctypes.c_void_p
+    fake = P(16)
+    rows = lib.dllm_transfer_threshold_rows
+    assert rows(fake, P(24), None, 2, 4, 0, P(32), None) == -1 and "taus" in _err(lib)
+    assert rows(fake, P(24), P(32), 2, 4, 0, P(32), None) == -1 and "alias" in _err(lib)
+    assert rows(fake, P(24), None, 0, 4, 0, P(32), None) == 0
+    rules = (dc._CRule * 1)()
+    rules[0].kind, rules[0].mask, rules[0].out, rules[0].k = dc.RULE_TOPK, 96, 128, 160
+    rules[0].taus = 200                               # only threshold takes taus
+    assert lib.dllm_token_stats(fake, 1, 1, 4, 8, 8, 0.0, 0, 0, None, 0, fake, P(24), P(40),
+                                None, rules, 1, fake, 1 << 20, None) == -1
+    assert "per-row" in _err(lib)
+    with pytest.raises(ValueError):
+        import torch
+        dc.Rule(dc.RULE_FACTOR, None, torch.zeros(2, dtype=torch.float64))
+
+
 def test_transfer_argument_errors(lib):
     fake = ctypes.c_void_p(16)
     assert lib.dllm_transfer_threshold(fake, fake, 1, 4, math.nan, 0, ctypes.c_void_p(32), None) == -1
