@@ -244,8 +244,12 @@ __device__ inline void short_rank_rule(const RuleDev &r, int b, int L, const flo
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, nw = blockDim.x >> 6;
   const uint8_t *m_row = r.mask + (int64_t)b * L;
   uint8_t *o_row = r.out + (int64_t)b * L;
+  // the score is loaded whatever the mask says, so both loads are in flight
+  // together (one memory round trip, not two)
+  const float cv = t < L ? rule_conf(r, conf + (int64_t)b * L + t) : 0.f;
+  const int kq = r.kind == DLLM_RULE_TOPK ? r.k[b] : 0;     // in flight with the row's loads
   const bool cand = t < L && m_row[t];
-  const float c = cand ? conf_sanitized(rule_conf(r, conf + (int64_t)b * L + t)) : 0.f;
+  const float c = cand ? conf_sanitized(cv) : 0.f;
   const uint64_t key = cand ? (((uint64_t)conf_key(c) << 32) | (uint32_t)t) : kSentinel;
   int *wcnt = sm.misc, *wfail = sm.misc + 32;
   const uint64_t m = __builtin_amdgcn_ballot_w64(cand);
@@ -255,6 +259,27 @@ __device__ inline void short_rank_rule(const RuleDev &r, int b, int L, const flo
   const int n = slots_sum(wcnt, nw, wave, &off);
   if (cand) sm.keys[off + lane_prefix(m)] = key;
   __syncthreads();
+  if (n <= 64) {
+    // One wave ranks every candidate and finds the first failure; the other
+    // waves only clear their own non-candidates, so no further barrier.
+    if (t < L && !cand) o_row[t] = 0;
+    if (wave != 0) return;
+    const bool own = lane < n;
+    const uint64_t qk = own ? sm.keys[lane] : kSentinel;
+    int rk = 0;
+    double unused1;
+    if (own) count_below<false>(qk, sm.keys, nullptr, 0, n, rk, unused1);
+    int nc1;
+    if (r.kind == DLLM_RULE_TOPK) {
+      nc1 = kq < 0 ? 0 : (kq > n ? n : kq);
+    } else {
+      const bool fails = own && !factor_holds(rk, conf_from_key((uint32_t)(qk >> 32)), r.param);
+      const int first = wave_min_i(fails ? rk : 0x7fffffff);
+      nc1 = n ? max(first < n ? first : n, 1) : 0;
+    }
+    if (own) o_row[(uint32_t)qk] = rk < nc1 ? 1 : 0;
+    return;
+  }
   const int P = owners_for(n, blockDim.x);
   double unused;
   uint64_t q;
@@ -262,8 +287,7 @@ __device__ inline void short_rank_rule(const RuleDev &r, int b, int L, const flo
   const bool owner = t < n;     // thread t < n owns query t
   int n_commit;
   if (r.kind == DLLM_RULE_TOPK) {
-    const int k = r.k[b];
-    n_commit = k < 0 ? 0 : (k > n ? n : k);
+    n_commit = kq < 0 ? 0 : (kq > n ? n : kq);
   } else {
     const bool fails = owner && !factor_holds(rank, conf_from_key((uint32_t)(q >> 32)), r.param);
     const int wmin = wave_min_i(fails ? rank : 0x7fffffff);
@@ -288,8 +312,9 @@ __device__ inline bool short_entropy_rule(const RuleDev &r, int b, int L, const 
   const int t = threadIdx.x, nt = blockDim.x, lane = t & 63, wave = t >> 6, nw = nt >> 6;
   const uint8_t *m_row = r.mask + (int64_t)b * L;
   uint8_t *o_row = r.out + (int64_t)b * L;
+  const float hv = t < L ? load_coherent(ent + (int64_t)b * L + t) : 0.f;   // with the mask
   const bool cand = t < L && m_row[t];
-  const float h = cand ? load_coherent(ent + (int64_t)b * L + t) : 0.f;
+  const float h = cand ? hv : 0.f;
   const uint32_t u = __float_as_uint(h);
   const bool bad = cand && u != 0x80000000u && (!bits_finite(u) || (u & 0x80000000u) != 0);
   const uint64_t key = cand ? (((uint64_t)ent_key(h) << 32) | (uint32_t)t) : kSentinel;
@@ -327,6 +352,42 @@ __device__ inline bool short_entropy_rule(const RuleDev &r, int b, int L, const 
   // queries: every key of F, then the smallest key above gamma (index nF)
   const bool has_next = nxt != kSentinel;
   const int nq = nF + (has_next ? 1 : 0);
+  if (nq <= 64) {
+    // One wave ranks every query, sums the prefixes and finds the first
+    // failure; the other waves only clear their own positions, so no further
+    // barrier.
+    if (above && key != nxt) o_row[t] = 0;
+    if (t < L && !cand) o_row[t] = 0;
+    if (wave != 0) return true;
+    const bool lv = lane < nq;
+    const uint64_t qk = lane < nF ? sm.keys[lane] : (lv ? nxt : kSentinel);
+    int rk = 0;
+    double Sq = 0.0;
+    if (lv) count_below<true>(qk, sm.keys, sm.hs, 0, nF, rk, Sq);
+    const double err1 = (double)(nF + 64) * 0x1p-52 * Sq;
+    const bool unc = lv && r.gamma_class == 0 && err1 != 0.0 && fabs(Sq - r.param) <= err1;
+    const bool fl = lv && !ent_prefix_ok(r, Sq <= r.param, 0, 0);
+    int first1 = wave_min_i(fl ? rk : 0x7fffffff);
+    if (__builtin_amdgcn_ballot_w64(unc) != 0) {
+      // rare: decide the prefixes exactly, walking the queries in rank order
+      // (every lane runs the same wave-uniform walk)
+      const uint32_t hbits = __float_as_uint(ent_from_key((uint32_t)(qk >> 32)));
+      Fx acc;
+      fx_zero(acc);
+      int upto = nq;
+      for (int i = 0; i < nq; ++i) {
+        if (!fx_le(acc, r.gamma_fx)) { upto = i; break; }
+        const uint64_t who = __builtin_amdgcn_ballot_w64(lv && rk == i);
+        const uint32_t hb = __builtin_amdgcn_readlane(hbits, (int)__builtin_ctzll(who));
+        fx_add(acc, fx_from_f32_bits(hb));
+      }
+      first1 = upto < nq ? upto : 0x7fffffff;
+    }
+    const int ns1 = first1 != 0x7fffffff ? first1 : min(nF + 1, nc);
+    const int ncm1 = nc ? max(ns1, 1) : 0;
+    if (lv) o_row[(uint32_t)qk] = rk < ncm1 ? 1 : 0;
+    return true;
+  }
   const int P = owners_for(nq, nt);
   double S;
   uint64_t q;
@@ -402,8 +463,8 @@ __device__ inline int sort_candidates(const RuleDev &r, int b, int L, const floa
   int mine = 0;
   for (int i = tid; i < Np; i += nt) {
     uint64_t key = kSentinel;
+    const float v = i < L ? (by_entropy ? load_coherent(s_row + i) : rule_conf(r, s_row + i)) : 0.f;
     if (i < L && m_row[i]) {
-      const float v = by_entropy ? load_coherent(s_row + i) : rule_conf(r, s_row + i);
       const uint32_t hk = by_entropy ? ent_key(v) : conf_key(v);
       key = ((uint64_t)hk << 32) | (uint32_t)i;
       ++mine;
@@ -493,8 +554,9 @@ __device__ inline void rule_threshold(const RuleDev &r, int b, int L, const floa
   uint64_t my_best = kSentinel;
   for (int l = tid; l < L; l += nt) {
     uint8_t v = 0;
+    const float cv = rule_conf(r, c_row + l);
     if (m_row[l]) {
-      const float c = conf_sanitized(rule_conf(r, c_row + l));
+      const float c = conf_sanitized(cv);
       const double cd = (double)c;
       v = (r.strict ? (cd > tau) : (cd >= tau)) ? 1 : 0;
       my_pass += v;

@@ -693,15 +693,14 @@ __device__ __forceinline__ bool finalize_partial(const Partial &p, float c, RowR
 // Writes one row's statistics (coherent: the batch-row finisher and the
 // rules read them) and decides its edit; returns 1 if the row was edited.
 __device__ __forceinline__ int publish_row(const StatsArgs &a, int64_t row_id,
-                                           const RowResult &res) {
+                                           const RowResult &res, uint8_t edit_m, int32_t edit_t) {
   store_coherent(&a.x0[row_id], res.x0);
   store_coherent(&a.prob[row_id], res.prob);
   store_coherent(&a.entropy[row_id], res.ent);
   if (a.margin) store_coherent(&a.margin[row_id], res.margin);
   if (a.argmax) a.argmax[row_id] = res.argmax;
   if (!a.has_edit) return 0;
-  const uint8_t e = edit_decision(a.edit_mask[row_id], res.x0, a.edit_tokens[row_id],
-                                  res.prob, a.edit_tau);
+  const uint8_t e = edit_decision(edit_m, res.x0, edit_t, res.prob, a.edit_tau);
   a.edit_out[row_id] = e;
   if (e && a.canvas) a.canvas[row_id] = res.x0;      // this row's own token
   return e;
@@ -716,6 +715,9 @@ __device__ inline void finish_canvas(const StatsArgs &a, uint32_t b, int edits) 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
   const int64_t L = a.L, base = (int64_t)b * L;
   int left = 0;
+  // The rule's output of a position was written by whichever thread owned it
+  // in the ranking: make every write visible before reading them back.
+  __syncthreads();
   if (a.n_rank_rules) {
     const RuleDev &r = a.rank_rules[0];
     for (int64_t l = tid; l < L; l += blockDim.x) {
@@ -800,6 +802,16 @@ __global__ __launch_bounds__(NT) void token_stats_kernel(StatsArgs a) {
     return;
   }
 
+  // The edit rule's inputs for this row, loaded before the stream so that
+  // their latency hides behind it (the tokens are read before any write of
+  // this launch, as they would be at publication).
+  uint8_t edit_m = 0;
+  int32_t edit_t = 0;
+  if (tid == 0 && a.has_edit) {
+    edit_m = a.edit_mask[row_id];
+    edit_t = a.edit_tokens[row_id];
+  }
+
   stream_slice<T, NT, UV, SAMPLE, VECLOAD, FULL>(a, row, lo, hi, b, l, wave_parts,
                                                  &slice_parts_acc);
 
@@ -844,7 +856,8 @@ __global__ __launch_bounds__(NT) void token_stats_kernel(StatsArgs a) {
   if (tid == 0) s_slow = !finalize_partial<SAMPLE>(slice_parts_acc, a.c2, res);
   __syncthreads();
   if (s_slow) res = slow_row<T, NT, SAMPLE>(a, row, b, l, slow_scratch);
-  if (tid == 0 && publish_row(a, row_id, res) && a.counts) atomicAdd(&a.edit_count[b], 1u);
+  if (tid == 0 && publish_row(a, row_id, res, edit_m, edit_t) && a.counts)
+    atomicAdd(&a.edit_count[b], 1u);
   finish_row(a, b, smem);
 }
 
