@@ -350,6 +350,39 @@ __device__ __forceinline__ void merge_sample(Partial &a, const Partial &b) {
   if (b.sb > a.sb || (b.sb == a.sb && b.ib < a.ib)) { a.sb = b.sb; a.ib = b.ib; a.xb = b.xb; }
 }
 
+__device__ __forceinline__ Partial empty_partial() {
+  Partial p;
+  p.M = -kInf; p.idx = kIdxNone; p.z = 0.f; p.S = 0.f;
+  p.sb = -kInf; p.ib = kIdxNone; p.xb = -kInf; p.R2 = -kInf;
+  return p;
+}
+
+// Butterfly merge over the partials of lanes [0, n) of a wave (n a power of
+// two, at most 64): log2(n) rounds instead of n - 1 dependent merges.  Both
+// merges give the same bits whichever side a partial is on, so every lane of
+// the group ends with the same, launch-independent result.
+template <bool SAMPLE>
+__device__ __forceinline__ Partial butterfly_merge(Partial q, int n, float c) {
+  for (int off = 1; off < n; off <<= 1) {
+    Partial o;
+    o.M = __shfl_xor(q.M, off);
+    o.idx = __shfl_xor(q.idx, off);
+    o.z = __shfl_xor(q.z, off);
+    o.S = __shfl_xor(q.S, off);
+    o.R2 = __shfl_xor(q.R2, off);
+    if constexpr (SAMPLE) {
+      o.sb = __shfl_xor(q.sb, off);
+      o.ib = __shfl_xor(q.ib, off);
+      o.xb = __shfl_xor(q.xb, off);
+    } else {
+      o.sb = -kInf; o.ib = kIdxNone; o.xb = -kInf;
+    }
+    merge_partial(q, o, c);
+    if constexpr (SAMPLE) merge_sample(q, o);
+  }
+  return q;
+}
+
 __device__ __forceinline__ bool is_suppressed(const StatsArgs &a, int64_t v) {
   for (int i = 0; i < a.n_suppress; ++i)
     if (a.suppress[i] == v) return true;
@@ -535,13 +568,11 @@ __device__ void stream_slice(const StatsArgs &a, const T *row, int64_t lo, int64
   }
   if (lane == 0) wave_parts[wave] = p;
   __syncthreads();
-  if (tid == 0) {
-    Partial acc = wave_parts[0];
-    for (int w = 1; w < NT / 64; ++w) {
-      merge_partial(acc, wave_parts[w], a.c2);
-      if constexpr (SAMPLE) merge_sample(acc, wave_parts[w]);
-    }
-    *out = acc;
+  if (wave == 0) {
+    constexpr int NW = NT / 64;
+    const Partial acc =
+        butterfly_merge<SAMPLE>(lane < NW ? wave_parts[lane] : empty_partial(), NW, a.c2);
+    if (lane == 0) *out = acc;
   }
 }
 
@@ -669,7 +700,7 @@ __device__ __forceinline__ bool row_needed(const StatsArgs &a, int64_t row_id) {
 // Statistics of a finished row from its merged partial; false when the row is
 // degenerate (NaN, +inf, or no finite unsuppressed logit) and needs the
 // two-pass path.
-template <bool SAMPLE>
+template <bool SAMPLE, bool FULL>
 __device__ __forceinline__ bool finalize_partial(const Partial &p, float c, RowResult &res) {
   const bool ok = bits_finite(__float_as_uint(p.M)) && bits_finite(__float_as_uint(p.z)) &&
                   bits_finite(__float_as_uint(p.S)) &&
@@ -677,7 +708,8 @@ __device__ __forceinline__ bool finalize_partial(const Partial &p, float c, RowR
   if (ok) {
     const float zf = 1.0f + p.z;
     res.ent = log1pf(p.z) - kLn2 * p.S / zf;
-    res.margin = -expm1f((p.R2 - p.M) * c * kLn2) / zf;   // (1 - e^((runner-up - max)/Ts)) / z
+    // (1 - e^((runner-up - max)/Ts)) / z; only the FULL kernels track the runner-up
+    res.margin = FULL ? -expm1f((p.R2 - p.M) * c * kLn2) / zf : 0.f;
     res.argmax = p.idx;
     if (SAMPLE) {
       res.x0 = p.ib;
@@ -837,14 +869,21 @@ __global__ __launch_bounds__(NT) void token_stats_kernel(StatsArgs a) {
       w[1] = make_uint4(0u, 0u, 0u, 0u);
     }
     __syncthreads();
-    if (tid == 0) {
-      Partial acc = lds[0];
-      for (int s = 1; s < a.slices; ++s) {       // fixed slice order: reproducible
+    if (tid < 64) {
+      // lane l merges slices l, l + 64, ... in order, then a butterfly over
+      // the lanes: a fixed order, so results are reproducible
+      Partial acc = tid < a.slices ? lds[tid] : empty_partial();
+      for (int s = tid + 64; s < a.slices; s += 64) {
         merge_partial(acc, lds[s], a.c2);
         if (SAMPLE) merge_sample(acc, lds[s]);
       }
-      slice_parts_acc = acc;
-      a.row_count[row_id] = 0u;
+      int n = 1;
+      while (n < a.slices && n < 64) n <<= 1;
+      acc = butterfly_merge<SAMPLE>(acc, n, a.c2);
+      if (tid == 0) {
+        slice_parts_acc = acc;
+        a.row_count[row_id] = 0u;
+      }
     }
     __syncthreads();
   }
@@ -853,7 +892,7 @@ __global__ __launch_bounds__(NT) void token_stats_kernel(StatsArgs a) {
   __shared__ int s_slow;
   RowResult res;
   res.x0 = 0; res.prob = 0.f; res.ent = 0.f; res.margin = 0.f; res.argmax = 0;
-  if (tid == 0) s_slow = !finalize_partial<SAMPLE>(slice_parts_acc, a.c2, res);
+  if (tid == 0) s_slow = !finalize_partial<SAMPLE, FULL>(slice_parts_acc, a.c2, res);
   __syncthreads();
   if (s_slow) res = slow_row<T, NT, SAMPLE>(a, row, b, l, slow_scratch);
   if (tid == 0 && publish_row(a, row_id, res, edit_m, edit_t) && a.counts)
