@@ -166,6 +166,25 @@ __device__ __forceinline__ void count_below(uint64_t q, const uint64_t *keys, co
   int c0 = 0, c1 = 0;
   double s0 = 0.0, s1 = 0.0;
   int j = j0;
+  for (; j + 8 <= j1; j += 8) {
+    uint64_t kk[8];
+    double vv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      kk[u] = keys[j + u];
+      if constexpr (VALS) vv[u] = vals[j + u];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; u += 2) {
+      const bool la = kk[u] < q, lb = kk[u + 1] < q;
+      c0 += (int)la;
+      c1 += (int)lb;
+      if constexpr (VALS) {
+        s0 += la ? vv[u] : 0.0;
+        s1 += lb ? vv[u + 1] : 0.0;
+      }
+    }
+  }
   for (; j + 4 <= j1; j += 4) {
     const uint64_t k0 = keys[j], k1 = keys[j + 1], k2 = keys[j + 2], k3 = keys[j + 3];
     const bool l0 = k0 < q, l1 = k1 < q, l2 = k2 < q, l3 = k3 < q;
