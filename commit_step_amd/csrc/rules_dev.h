@@ -57,7 +57,7 @@ __host__ __device__ inline int rule_pow2(int L) {
 // threads.
 __host__ __device__ inline size_t rule_smem_bytes(int L, int nt) {
   const size_t Np = (size_t)rule_pow2(L);
-  const size_t lists = Np * 16 + (size_t)nt * 12;   // short rows
+  const size_t lists = Np * 20 + (size_t)nt * 12;   // short rows (lists, x0 per position)
   const size_t keys = Np * 8;                        // sorting network
   return (((lists > keys ? lists : keys) + 7) & ~(size_t)7) + 512;
 }
@@ -67,6 +67,7 @@ struct RuleSmem {
   double *hs;         // [Np] values matching the list (short rows)
   double *part_sum;   // [nt]
   int *part_cnt;      // [nt]
+  int32_t *x0s;       // [Np] x0 of every position (short rows with a canvas)
   int *misc;          // [128]
 };
 
@@ -77,7 +78,8 @@ __device__ inline RuleSmem rule_smem(unsigned char *base, int L) {
   s.hs = reinterpret_cast<double *>(base + Np * 8);
   s.part_sum = reinterpret_cast<double *>(base + Np * 16);
   s.part_cnt = reinterpret_cast<int *>(base + Np * 16 + nt * 8);
-  const size_t lists = Np * 16 + nt * 12;
+  s.x0s = reinterpret_cast<int32_t *>(base + Np * 16 + nt * 12);
+  const size_t lists = Np * 20 + nt * 12;
   const size_t top = lists > Np * 8 ? lists : Np * 8;
   s.misc = reinterpret_cast<int *>(base + ((top + 7) & ~(size_t)7));
   return s;
@@ -86,6 +88,24 @@ __device__ inline RuleSmem rule_smem(unsigned char *base, int L) {
 __device__ __forceinline__ float load_coherent(const float *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ int32_t load_coherent_i32(const int32_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Where a rank rule's commits go besides its mask: inside the canvas step,
+// x0 is written into the batch row's canvas at every committed position as
+// the rule decides it (no second pass over the mask).  Both pointers are the
+// batch row's own (position l at [l]); canvas is null outside the canvas step.
+struct CommitSink {
+  int32_t *canvas;
+  const int32_t *x0;      // published by this launch: read with coherent loads
+};
+
+// Candidates of the batch row and how many the rule committed (thread 0).
+struct RuleCount {
+  int nc;
+  int committed;
+};
 
 // A ranking rule's confidence from its score array (negated for a negative
 // entropy; NaN stays NaN and counts as -inf).
@@ -258,8 +278,8 @@ __device__ __forceinline__ int slots_sum(const int *slots, int nw, int wave, int
 }
 
 // topk / factor on a short row.
-__device__ inline void short_rank_rule(const RuleDev &r, int b, int L, const float *conf,
-                                       const RuleSmem &sm) {
+__device__ inline RuleCount short_rank_rule(const RuleDev &r, int b, int L, const float *conf,
+                                            const RuleSmem &sm, const CommitSink &sk) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, nw = blockDim.x >> 6;
   const uint8_t *m_row = r.mask + (int64_t)b * L;
   uint8_t *o_row = r.out + (int64_t)b * L;
@@ -267,6 +287,7 @@ __device__ inline void short_rank_rule(const RuleDev &r, int b, int L, const flo
   // together (one memory round trip, not two)
   const float cv = t < L ? rule_conf(r, conf + (int64_t)b * L + t) : 0.f;
   const int kq = r.kind == DLLM_RULE_TOPK ? r.k[b] : 0;     // in flight with the row's loads
+  if (sk.canvas && t < L) sm.x0s[t] = load_coherent_i32(sk.x0 + t);
   const bool cand = t < L && m_row[t];
   const float c = cand ? conf_sanitized(cv) : 0.f;
   const uint64_t key = cand ? (((uint64_t)conf_key(c) << 32) | (uint32_t)t) : kSentinel;
@@ -282,7 +303,7 @@ __device__ inline void short_rank_rule(const RuleDev &r, int b, int L, const flo
     // One wave ranks every candidate and finds the first failure; the other
     // waves only clear their own non-candidates, so no further barrier.
     if (t < L && !cand) o_row[t] = 0;
-    if (wave != 0) return;
+    if (wave != 0) return RuleCount{n, 0};
     const bool own = lane < n;
     const uint64_t qk = own ? sm.keys[lane] : kSentinel;
     int rk = 0;
@@ -296,8 +317,12 @@ __device__ inline void short_rank_rule(const RuleDev &r, int b, int L, const flo
       const int first = wave_min_i(fails ? rk : 0x7fffffff);
       nc1 = n ? max(first < n ? first : n, 1) : 0;
     }
-    if (own) o_row[(uint32_t)qk] = rk < nc1 ? 1 : 0;
-    return;
+    if (own) {
+      const bool c1 = rk < nc1;
+      o_row[(uint32_t)qk] = c1 ? 1 : 0;
+      if (c1 && sk.canvas) sk.canvas[(uint32_t)qk] = sm.x0s[(uint32_t)qk];
+    }
+    return RuleCount{n, nc1};
   }
   const int P = owners_for(n, blockDim.x);
   double unused;
@@ -316,8 +341,13 @@ __device__ inline void short_rank_rule(const RuleDev &r, int b, int L, const flo
     for (int w = 0; w < nw; ++w) first = min(first, wfail[w]);
     n_commit = n ? max(first < n ? first : n, 1) : 0;
   }
-  if (owner) o_row[(uint32_t)q] = rank < n_commit ? 1 : 0;
+  if (owner) {
+    const bool c1 = rank < n_commit;
+    o_row[(uint32_t)q] = c1 ? 1 : 0;
+    if (c1 && sk.canvas) sk.canvas[(uint32_t)q] = sm.x0s[(uint32_t)q];
+  }
   if (t < L && !cand) o_row[t] = 0;
+  return RuleCount{n, n_commit};
 }
 
 // entropy_bound on a short row.  Returns false (nothing written, every thread
@@ -327,11 +357,13 @@ __device__ inline void short_rank_rule(const RuleDev &r, int b, int L, const flo
 // followed by another committed one, so ranks and prefix sums run over that
 // subset F plus the smallest key above gamma.
 __device__ inline bool short_entropy_rule(const RuleDev &r, int b, int L, const float *ent,
-                                          const RuleSmem &sm) {
+                                          const RuleSmem &sm, const CommitSink &sk,
+                                          RuleCount &rc) {
   const int t = threadIdx.x, nt = blockDim.x, lane = t & 63, wave = t >> 6, nw = nt >> 6;
   const uint8_t *m_row = r.mask + (int64_t)b * L;
   uint8_t *o_row = r.out + (int64_t)b * L;
   const float hv = t < L ? load_coherent(ent + (int64_t)b * L + t) : 0.f;   // with the mask
+  if (sk.canvas && t < L) sm.x0s[t] = load_coherent_i32(sk.x0 + t);
   const bool cand = t < L && m_row[t];
   const float h = cand ? hv : 0.f;
   const uint32_t u = __float_as_uint(h);
@@ -377,6 +409,7 @@ __device__ inline bool short_entropy_rule(const RuleDev &r, int b, int L, const 
     // barrier.
     if (above && key != nxt) o_row[t] = 0;
     if (t < L && !cand) o_row[t] = 0;
+    rc = RuleCount{nc, 0};
     if (wave != 0) return true;
     const bool lv = lane < nq;
     const uint64_t qk = lane < nF ? sm.keys[lane] : (lv ? nxt : kSentinel);
@@ -404,7 +437,12 @@ __device__ inline bool short_entropy_rule(const RuleDev &r, int b, int L, const 
     }
     const int ns1 = first1 != 0x7fffffff ? first1 : min(nF + 1, nc);
     const int ncm1 = nc ? max(ns1, 1) : 0;
-    if (lv) o_row[(uint32_t)qk] = rk < ncm1 ? 1 : 0;
+    if (lv) {
+      const bool c1 = rk < ncm1;
+      o_row[(uint32_t)qk] = c1 ? 1 : 0;
+      if (c1 && sk.canvas) sk.canvas[(uint32_t)qk] = sm.x0s[(uint32_t)qk];
+    }
+    rc = RuleCount{nc, ncm1};
     return true;
   }
   const int P = owners_for(nq, nt);
@@ -441,9 +479,14 @@ __device__ inline bool short_entropy_rule(const RuleDev &r, int b, int L, const 
   // fails (its prefix holds an entropy above gamma), or the row ends.
   const int n_star = first != 0x7fffffff ? first : min(nF + 1, nc);
   const int n_commit = nc ? max(n_star, 1) : 0;
-  if (live) o_row[(uint32_t)q] = rank < n_commit ? 1 : 0;
+  if (live) {
+    const bool c1 = rank < n_commit;
+    o_row[(uint32_t)q] = c1 ? 1 : 0;
+    if (c1 && sk.canvas) sk.canvas[(uint32_t)q] = sm.x0s[(uint32_t)q];
+  }
   if (above && key != nxt) o_row[t] = 0;
   if (t < L && !cand) o_row[t] = 0;
+  rc = RuleCount{nc, n_commit};
   return true;
 }
 
@@ -498,17 +541,22 @@ __device__ inline int sort_candidates(const RuleDev &r, int b, int L, const floa
 }
 
 // Commit the first n of the nc sorted candidates; zero every other position.
-__device__ inline void commit_sorted(const RuleDev &r, int b, int L, int n, int nc,
-                                     const RuleSmem &sm) {
+__device__ inline RuleCount commit_sorted(const RuleDev &r, int b, int L, int n, int nc,
+                                          const RuleSmem &sm, const CommitSink &sk) {
   uint8_t *o_row = r.out + (int64_t)b * L;
   const uint8_t *m_row = r.mask + (int64_t)b * L;
-  for (int i = threadIdx.x; i < nc; i += blockDim.x) o_row[(uint32_t)sm.keys[i]] = i < n ? 1 : 0;
+  for (int i = threadIdx.x; i < nc; i += blockDim.x) {
+    const uint32_t pos = (uint32_t)sm.keys[i];
+    o_row[pos] = i < n ? 1 : 0;
+    if (i < n && sk.canvas) sk.canvas[pos] = load_coherent_i32(sk.x0 + pos);
+  }
   for (int l = threadIdx.x; l < L; l += blockDim.x)
     if (!m_row[l]) o_row[l] = 0;
+  return RuleCount{nc, n};
 }
 
-__device__ inline void long_rank_rule(const RuleDev &r, int b, int L, const float *conf,
-                                      const RuleSmem &sm) {
+__device__ inline RuleCount long_rank_rule(const RuleDev &r, int b, int L, const float *conf,
+                                           const RuleSmem &sm, const CommitSink &sk) {
   const int nc = sort_candidates(r, b, L, conf, false, sm);
   int n;
   if (r.kind == DLLM_RULE_TOPK) {
@@ -524,13 +572,13 @@ __device__ inline void long_rank_rule(const RuleDev &r, int b, int L, const floa
     __syncthreads();
     n = nc ? max(*first_fail, 1) : 0;
   }
-  commit_sorted(r, b, L, n, nc, sm);
+  return commit_sorted(r, b, L, n, nc, sm, sk);
 }
 
 // entropy_bound on the sorted candidates, for any entropies (NaN counts as
 // +inf): exact sequential walk in fixed point by one thread.
-__device__ inline void long_entropy_rule(const RuleDev &r, int b, int L, const float *ent,
-                                         const RuleSmem &sm) {
+__device__ inline RuleCount long_entropy_rule(const RuleDev &r, int b, int L, const float *ent,
+                                              const RuleSmem &sm, const CommitSink &sk) {
   const int nc = sort_candidates(r, b, L, ent, true, sm);
   int *first_fail = sm.misc + 6;
   if (threadIdx.x == 0) {
@@ -554,27 +602,30 @@ __device__ inline void long_entropy_rule(const RuleDev &r, int b, int L, const f
   }
   __syncthreads();
   const int n = nc ? max(*first_fail, 1) : 0;
-  commit_sorted(r, b, L, n, nc, sm);
+  return commit_sorted(r, b, L, n, nc, sm, sk);
 }
 
 // threshold: no ranking needed.
-__device__ inline void rule_threshold(const RuleDev &r, int b, int L, const float *conf,
-                                      const RuleSmem &sm) {
+__device__ inline RuleCount rule_threshold(const RuleDev &r, int b, int L, const float *conf,
+                                           const RuleSmem &sm, const CommitSink &sk) {
   const int tid = threadIdx.x, nt = blockDim.x;
   unsigned long long *best = reinterpret_cast<unsigned long long *>(sm.misc + 24);
   int *n_pass = sm.misc + 2;
-  if (tid == 0) { *best = kSentinel; *n_pass = 0; }
+  int *n_cand = sm.misc + 3;
+  if (tid == 0) { *best = kSentinel; *n_pass = 0; *n_cand = 0; }
   __syncthreads();
   const float *c_row = conf + (int64_t)b * L;
   const uint8_t *m_row = r.mask + (int64_t)b * L;
   uint8_t *o_row = r.out + (int64_t)b * L;
   const double tau = r.taus ? r.taus[b] : r.param;
-  int my_pass = 0;
+  int my_pass = 0, my_cand = 0;
   uint64_t my_best = kSentinel;
   for (int l = tid; l < L; l += nt) {
     uint8_t v = 0;
     const float cv = rule_conf(r, c_row + l);
+    const int32_t xv = sk.canvas ? load_coherent_i32(sk.x0 + l) : 0;
     if (m_row[l]) {
+      ++my_cand;
       const float c = conf_sanitized(cv);
       const double cd = (double)c;
       v = (r.strict ? (cd > tau) : (cd >= tau)) ? 1 : 0;
@@ -583,33 +634,45 @@ __device__ inline void rule_threshold(const RuleDev &r, int b, int L, const floa
       my_best = key < my_best ? key : my_best;
     }
     o_row[l] = v;
+    if (v && sk.canvas) sk.canvas[l] = xv;
   }
   if (my_pass) atomicAdd(n_pass, my_pass);
+  if (my_cand) atomicAdd(n_cand, my_cand);
   if (my_best != kSentinel) atomicMin(best, (unsigned long long)my_best);
   __syncthreads();
-  if (tid == 0 && *n_pass == 0 && *best != kSentinel) o_row[(uint32_t)*best] = 1;
+  RuleCount rc{*n_cand, *n_pass};
+  if (tid == 0 && *n_pass == 0 && *best != kSentinel) {
+    const uint32_t pos = (uint32_t)*best;
+    o_row[pos] = 1;
+    if (sk.canvas) sk.canvas[pos] = load_coherent_i32(sk.x0 + pos);
+    rc.committed = 1;
+  }
+  return rc;
 }
 
 // Runs a ranking rule on batch row b.  Every thread of the workgroup must call
 // it.  `conf` is the confidence (prob) array and `ent` the entropy array.
-__device__ inline void run_batch_rule(const RuleDev &r, int b, int L, const float *conf,
-                                      const float *ent, unsigned char *smem) {
+// Returns the candidate and commit counts (valid in thread 0).
+__device__ inline RuleCount run_batch_rule(const RuleDev &r, int b, int L, const float *conf,
+                                           const float *ent, unsigned char *smem,
+                                           const CommitSink &sk) {
   const RuleSmem sm = rule_smem(smem, L);
   const bool short_row = L <= (int)blockDim.x;
+  RuleCount rc{0, 0};
   switch (r.kind) {
     case DLLM_RULE_THRESHOLD:
-      rule_threshold(r, b, L, conf, sm);
+      rc = rule_threshold(r, b, L, conf, sm, sk);
       break;
     case DLLM_RULE_TOPK:
     case DLLM_RULE_FACTOR:
-      if (short_row) short_rank_rule(r, b, L, conf, sm);
-      else long_rank_rule(r, b, L, conf, sm);
+      if (short_row) rc = short_rank_rule(r, b, L, conf, sm, sk);
+      else rc = long_rank_rule(r, b, L, conf, sm, sk);
       break;
     case DLLM_RULE_ENTROPY_BOUND: {
-      const bool done = short_row && short_entropy_rule(r, b, L, ent, sm);
+      const bool done = short_row && short_entropy_rule(r, b, L, ent, sm, sk, rc);
       if (!done) {
         __syncthreads();
-        long_entropy_rule(r, b, L, ent, sm);
+        rc = long_entropy_rule(r, b, L, ent, sm, sk);
       }
       break;
     }
@@ -617,6 +680,7 @@ __device__ inline void run_batch_rule(const RuleDev &r, int b, int L, const floa
       break;
   }
   __syncthreads();
+  return rc;
 }
 
 __device__ __forceinline__ uint8_t edit_decision(uint8_t editable, int32_t x0, int32_t tok,

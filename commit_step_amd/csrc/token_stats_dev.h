@@ -738,54 +738,36 @@ __device__ __forceinline__ int publish_row(const StatsArgs &a, int64_t row_id,
   return e;
 }
 
-// Canvas update for the committed positions of batch row b and its counts.
-// Runs in the workgroup that completed the batch row, after the rank rule
-// (whose output this workgroup has just written).  edits < 0: the edit count
-// is in the workspace.
-__device__ inline void finish_canvas(const StatsArgs &a, uint32_t b, int edits) {
-  __shared__ int s_left[16];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
-  const int64_t L = a.L, base = (int64_t)b * L;
-  int left = 0;
-  // The rule's output of a position was written by whichever thread owned it
-  // in the ranking: make every write visible before reading them back.
-  __syncthreads();
-  if (a.n_rank_rules) {
-    const RuleDev &r = a.rank_rules[0];
-    for (int64_t l = tid; l < L; l += blockDim.x) {
-      const bool committed = r.out[base + l] != 0;
-      if (committed && a.canvas) a.canvas[base + l] = load_coh(&a.x0[base + l]);
-      left += (r.mask[base + l] && !committed) ? 1 : 0;
-    }
+// Counts of batch row b: candidates the rank rule left uncommitted and
+// positions edited.  The rule has already written x0 into the canvas at the
+// positions it committed.  edits < 0: the edit count is in the workspace.
+__device__ inline void finish_counts(const StatsArgs &a, uint32_t b, int edits,
+                                     const RuleCount &rc) {
+  if (threadIdx.x != 0 || !a.counts) return;
+  if (edits < 0) {
+    edits = (int)load_coh(&a.edit_count[b]);
+    a.edit_count[b] = 0u;        // leave the workspace zeroed
   }
-  if (a.counts) {
-    const int w = wave_sum_i(left);
-    if (lane == 0) s_left[wave] = w;
-    __syncthreads();
-    if (tid == 0) {
-      int tot = 0;
-      for (int i = 0; i < nw; ++i) tot += s_left[i];
-      if (edits < 0) {
-        edits = (int)load_coh(&a.edit_count[b]);
-        a.edit_count[b] = 0u;        // leave the workspace zeroed
-      }
-      a.counts[2 * b] = tot;
-      a.counts[2 * b + 1] = edits;
-    }
-  }
+  a.counts[2 * b] = a.n_rank_rules ? rc.nc - rc.committed : 0;
+  a.counts[2 * b + 1] = edits;
 }
 
-// The batch row's statistics are all published: rank rules, canvas, counts.
+// The batch row's statistics are all published: rank rules (the first one
+// also updating the canvas), then the counts.
 __device__ inline void complete_batch_row(const StatsArgs &a, uint32_t b, unsigned char *smem,
                                           int edits) {
+  RuleCount rc0{0, 0};
   for (int r = 0; r < a.n_rank_rules; ++r) {
     const RuleDev &rule = a.rank_rules[r];
     const float *conf = rule.score == DLLM_SCORE_MARGIN        ? a.margin
                         : rule.score == DLLM_SCORE_NEG_ENTROPY ? a.entropy
                                                                : a.prob;
-    run_batch_rule(rule, (int)b, (int)a.L, conf, a.entropy, smem);
+    const CommitSink sk{r == 0 && a.canvas ? a.canvas + (int64_t)b * a.L : nullptr,
+                        a.x0 + (int64_t)b * a.L};
+    const RuleCount rc = run_batch_rule(rule, (int)b, (int)a.L, conf, a.entropy, smem, sk);
+    if (r == 0) rc0 = rc;
   }
-  if (a.canvas || a.counts) finish_canvas(a, b, edits);
+  finish_counts(a, b, edits, rc0);
   if (threadIdx.x == 0) a.batch_count[b] = 0u;   // leave the workspace zeroed
 }
 
