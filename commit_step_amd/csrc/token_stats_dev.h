@@ -39,6 +39,7 @@
 #pragma once
 
 #include <stdarg.h>
+#include <stddef.h>
 #include <string.h>
 
 #include <algorithm>
@@ -64,6 +65,9 @@ struct Partial {          // one row slice's statistics (workspace)
   float R2;               // runner-up: largest logit but one maximal element (-inf: none)
 };
 static_assert(sizeof(Partial) == 32, "Partial is zeroed as two 16-byte words");
+static_assert(offsetof(Partial, idx) == 4 && offsetof(Partial, S) == 12 &&
+                  offsetof(Partial, ib) == 20 && offsetof(Partial, R2) == 28,
+              "Partial moves as four (float, 32-bit) pairs");
 
 // Publishing to other workgroups of the same launch, which may run on other
 // XCDs (each with its own L2): values are written with agent-scope atomic
@@ -82,18 +86,26 @@ __device__ __forceinline__ V load_coh(const V *p) {
 }
 __device__ __forceinline__ void wait_stores_complete() { __builtin_amdgcn_s_waitcnt(0); }
 
+// A partial moves as four 64-bit coherent words (field pairs).
+__device__ __forceinline__ uint64_t pack2(uint32_t lo, uint32_t hi) {
+  return (uint64_t)lo | ((uint64_t)hi << 32);
+}
 __device__ __forceinline__ void store_partial(Partial *dst, const Partial &p) {
-  store_coherent(&dst->M, p.M); store_coherent(&dst->idx, p.idx);
-  store_coherent(&dst->z, p.z); store_coherent(&dst->S, p.S);
-  store_coherent(&dst->sb, p.sb); store_coherent(&dst->ib, p.ib);
-  store_coherent(&dst->xb, p.xb); store_coherent(&dst->R2, p.R2);
+  uint64_t *w = reinterpret_cast<uint64_t *>(dst);
+  store_coherent(&w[0], pack2(__float_as_uint(p.M), (uint32_t)p.idx));
+  store_coherent(&w[1], pack2(__float_as_uint(p.z), __float_as_uint(p.S)));
+  store_coherent(&w[2], pack2(__float_as_uint(p.sb), (uint32_t)p.ib));
+  store_coherent(&w[3], pack2(__float_as_uint(p.xb), __float_as_uint(p.R2)));
 }
 __device__ __forceinline__ Partial load_partial(const Partial *src) {
+  const uint64_t *w = reinterpret_cast<const uint64_t *>(src);
+  const uint64_t w0 = load_coh(&w[0]), w1 = load_coh(&w[1]);
+  const uint64_t w2 = load_coh(&w[2]), w3 = load_coh(&w[3]);
   Partial p;
-  p.M = load_coh(&src->M); p.idx = load_coh(&src->idx);
-  p.z = load_coh(&src->z); p.S = load_coh(&src->S);
-  p.sb = load_coh(&src->sb); p.ib = load_coh(&src->ib);
-  p.xb = load_coh(&src->xb); p.R2 = load_coh(&src->R2);
+  p.M = __uint_as_float((uint32_t)w0); p.idx = (int)(uint32_t)(w0 >> 32);
+  p.z = __uint_as_float((uint32_t)w1); p.S = __uint_as_float((uint32_t)(w1 >> 32));
+  p.sb = __uint_as_float((uint32_t)w2); p.ib = (int)(uint32_t)(w2 >> 32);
+  p.xb = __uint_as_float((uint32_t)w3); p.R2 = __uint_as_float((uint32_t)(w3 >> 32));
   return p;
 }
 
@@ -844,12 +856,7 @@ __global__ __launch_bounds__(NT) void token_stats_kernel(StatsArgs a) {
     __syncthreads();
     if (!s_flag) return;
     Partial *lds = reinterpret_cast<Partial *>(smem);    // [slices], before the rules use it
-    for (int s = tid; s < a.slices; s += NT) {
-      lds[s] = load_partial(&parts[s]);
-      uint4 *w = reinterpret_cast<uint4 *>(&parts[s]);   // leave the record zero-filled
-      w[0] = make_uint4(0u, 0u, 0u, 0u);
-      w[1] = make_uint4(0u, 0u, 0u, 0u);
-    }
+    for (int s = tid; s < a.slices; s += NT) lds[s] = load_partial(&parts[s]);
     __syncthreads();
     if (tid < 64) {
       // lane l merges slices l, l + 64, ... in order, then a butterfly over
@@ -879,6 +886,14 @@ __global__ __launch_bounds__(NT) void token_stats_kernel(StatsArgs a) {
   if (s_slow) res = slow_row<T, NT, SAMPLE>(a, row, b, l, slow_scratch);
   if (tid == 0 && publish_row(a, row_id, res, edit_m, edit_t) && a.counts)
     atomicAdd(&a.edit_count[b], 1u);
+  if (a.slices > 1) {
+    Partial *parts = &a.partials[row_id * a.slices];
+    for (int s = tid; s < a.slices; s += NT) {         // leave the records zero-filled
+      uint4 *w = reinterpret_cast<uint4 *>(&parts[s]);
+      w[0] = make_uint4(0u, 0u, 0u, 0u);
+      w[1] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
   finish_row(a, b, smem);
 }
 

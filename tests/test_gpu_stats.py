@@ -136,6 +136,33 @@ def test_nan_and_inf_rows(dtype, T):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("T", [0.0, 0.8])
+def test_special_rows_in_split_rows_with_a_rule(dtype, T):
+    """Degenerate rows (NaN, +-inf, all -inf) split across workgroups and
+    finished by the workgroup that completes their batch row, with a fused
+    rule on the same statistics."""
+    V = 20000
+    x = _special_rows(V)
+    arr = bf16_bits(x) if dtype == "bf16" else x
+    B, L = x.shape[0], x.shape[1]
+    cand = np.ones((B, L), dtype=bool)
+    cand[0, ::3] = False
+    for sup in ((), (1, 3, V - 1)):
+        log(f"split special rows {dtype} T={T} suppress={sup}")
+        r = dc.Rule.threshold(to_dev(cand), 0.5)
+        st = dc.token_stats(to_dev(arr, dtype), temperature=T, seed=7, step=1, suppress_ids=sup,
+                            rules=[r])
+        gpu = stats_np(st)
+        ref = oracle.token_stats(arr, dtype, temperature=T, seed=7, step=1, suppress_ids=sup)
+        assert_stats(gpu, ref, dtype, f"split special {dtype} T={T}", x0_exact=(T == 0.0),
+                     mask=(gpu[0] == ref.x0))
+        assert_stats(gpu, ref, dtype, "split special entropy", x0_exact=False,
+                     fields=("entropy",))
+        want = oracle.threshold_transfer(gpu[1], cand, 0.5)
+        assert np.array_equal(r.out.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_sparse_minus_inf_logits(dtype):
     """Masked vocabulary entries (-inf) scattered through otherwise finite rows,
     also next to a rising maximum: the fast path must keep every row finite."""
