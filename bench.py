@@ -43,9 +43,12 @@ def parse_args():
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain 1 GiB device copy (counter calibration)")
     p.add_argument("--workload", default="diffusiongemma_canvas",
-                   choices=["diffusiongemma_canvas", "llada_block_loop"],
-                   help="diffusiongemma_canvas (default, the headline step) or llada_block_loop "
-                        "(the 32-step LLaDA block with dllm_commit_step, candidate rows only)")
+                   choices=["diffusiongemma_canvas", "llada_block_loop", "tiny", "dream_canvas",
+                            "batched"],
+                   help="diffusiongemma_canvas (default, the headline step); llada_block_loop "
+                        "(the 32-step LLaDA block with dllm_commit_step); tiny (1 x 64 x 4096 "
+                        "fp32, threshold); dream_canvas (4 x 256 x 151936 bf16, Gumbel-max "
+                        "T = 0.7, factor); batched (32 x 512 x 126464 bf16, strict threshold)")
     return p.parse_args()
 
 
@@ -233,6 +236,86 @@ def llada_block_loop(args):
     print(json.dumps(line), flush=True)
 
 
+def fused_workload(args):
+    """One fused launch of dllm_token_stats with the configuration's rule,
+    timed like the headline step; logit GB/s against the 8 TB/s peak."""
+    import numpy as np
+    import torch
+
+    import commit_step_amd as dc
+    import workloads
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    if args.workload == "batched":
+        p = workloads.CONFIG_PARAMS[5]
+        B, L, V = p["B"], p["L"], p["V"]
+        copies = [torch.empty((B, L, V), dtype=torch.bfloat16, device=dev)]
+        for b in range(B):                      # 4 GiB: one batch row at a time
+            w = workloads.config5_batch_row(b)
+            copies[0][b].copy_(torch.from_numpy(w.logits[0].view(np.int16)).view(torch.bfloat16))
+        cand = torch.ones((B, L), dtype=torch.uint8, device=dev)
+        kind, param, strict, T, seed, sup = dc.RULE_THRESHOLD, p["tau"], int(p["strict"]), 0.0, 0, ()
+        dtype, esz, label = dc.DLLM_BF16, 2, "batched: fused token_stats (greedy) + threshold(0.95, strict)"
+    else:
+        w = workloads.config1() if args.workload == "tiny" else workloads.config3()
+        B, L, V = w.shape
+        f32 = w.dtype == "f32"
+        host = torch.from_numpy(w.logits) if f32 else \
+            torch.from_numpy(w.logits.view(np.int16)).view(torch.bfloat16)
+        R = max(1, args.rotate) if args.workload == "tiny" else 2
+        copies = [host.to(dev) for _ in range(R)]
+        cand = torch.from_numpy(w.cand).to(dev)
+        sup = tuple(w.suppress_ids)
+        if args.workload == "tiny":
+            kind, param, strict, T, seed = dc.RULE_THRESHOLD, w.params["tau"], int(w.params["strict"]), 0.0, 0
+            label = "tiny: fused token_stats (greedy, fp32) + threshold(0.9)"
+        else:
+            kind, param, strict, T, seed = dc.RULE_FACTOR, w.params["f"], 0, w.temperature, w.seed
+            label = "dream_canvas: fused token_stats (Gumbel-max T=0.7) + factor(1.0)"
+        dtype, esz = (dc.DLLM_F32, 4) if f32 else (dc.DLLM_BF16, 2)
+    x0 = torch.empty((B, L), dtype=torch.int32, device=dev)
+    prob = torch.empty((B, L), dtype=torch.float32, device=dev)
+    ent = torch.empty((B, L), dtype=torch.float32, device=dev)
+    out = torch.empty((B, L), dtype=torch.uint8, device=dev)
+    lib = dc.load_library()
+    ws = torch.zeros(max(int(lib.dllm_token_stats_workspace_size(dtype, B, L, V)), 256),
+                     dtype=torch.uint8, device=dev)
+    rules = (dc._CRule * 1)()
+    rules[0].kind, rules[0].mask, rules[0].out = kind, cand.data_ptr(), out.data_ptr()
+    rules[0].param, rules[0].strict = param, strict
+    supa = (ctypes.c_int32 * max(1, len(sup)))(*sup)
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    calls = [(c.data_ptr(), dtype, B, L, V, V, float(T), seed, 0, supa, len(sup), x0.data_ptr(),
+              prob.data_ptr(), ent.data_ptr(), None, rules, 1, ws.data_ptr(), ws.numel(), stream)
+             for c in copies]
+    fn = lib.dllm_token_stats
+    steps = args.steps if args.workload == "tiny" else max(1, args.steps // 5)
+    rc = 0
+    for i in range(max(1, args.warmup // 5)):
+        rc |= fn(*calls[i % len(calls)])
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        rc |= fn(*calls[i % len(calls)])
+    end.record()
+    torch.cuda.synchronize()
+    if rc:
+        raise RuntimeError(lib.dllm_last_error().decode())
+    ms = start.elapsed_time(end) / steps
+    logit_bytes = B * L * V * esz
+    gbs = logit_bytes / (ms * 1e-3) / 1e9
+    print(json.dumps({
+        "metric": "logit GB/s of the fused token_stats + rule launch", "value": round(gbs, 2),
+        "unit": "GB/s", "n_gpus": 1, "steps": steps, "us_per_launch": round(ms * 1e3, 3),
+        "higher_is_better": True, "dtype": "bf16" if esz == 2 else "f32", "data": "synthetic",
+        "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "positions_per_s": round(B * L / (ms * 1e-3), 1),
+        "config": {"workload": label, "B": B, "L": L, "V": V, "copies": len(copies)}}), flush=True)
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -245,6 +328,9 @@ def main():
         return
     if args.workload == "llada_block_loop":
         llada_block_loop(args)
+        return
+    if args.workload in ("tiny", "dream_canvas", "batched"):
+        fused_workload(args)
         return
 
     import numpy as np
