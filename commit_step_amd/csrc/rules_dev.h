@@ -69,11 +69,13 @@ struct RuleSmem {
   int *part_cnt;      // [nt]
   int32_t *x0s;       // [Np] x0 of every position (short rows with a canvas)
   int *misc;          // [128]
+  int nt;             // threads of the workgroup (a compile-time constant at every caller)
 };
 
-__device__ inline RuleSmem rule_smem(unsigned char *base, int L) {
+__device__ inline RuleSmem rule_smem(unsigned char *base, int L, int nt_) {
   RuleSmem s;
-  const size_t Np = (size_t)rule_pow2(L), nt = blockDim.x;
+  s.nt = nt_;
+  const size_t Np = (size_t)rule_pow2(L), nt = (size_t)nt_;
   s.keys = reinterpret_cast<uint64_t *>(base);
   s.hs = reinterpret_cast<double *>(base + Np * 8);
   s.part_sum = reinterpret_cast<double *>(base + Np * 16);
@@ -235,7 +237,7 @@ template <bool VALS>
 __device__ inline int block_rank(int nq, int n0, uint64_t extra, const uint64_t *list, int n,
                                  const double *vals, const RuleSmem &sm, int P, double &sum,
                                  uint64_t &query) {
-  const int t = threadIdx.x, G = blockDim.x / P, part = t / P, i = t - part * P;
+  const int t = threadIdx.x, G = sm.nt / P, part = t / P, i = t - part * P;
   const int per = (n + G - 1) / G;
   const int j0 = min(part * per, n), j1 = min(j0 + per, n);
   const uint64_t q = i < n0 ? list[i] : (i < nq ? extra : kSentinel);
@@ -280,7 +282,7 @@ __device__ __forceinline__ int slots_sum(const int *slots, int nw, int wave, int
 // topk / factor on a short row.
 __device__ inline RuleCount short_rank_rule(const RuleDev &r, int b, int L, const float *conf,
                                             const RuleSmem &sm, const CommitSink &sk) {
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, nw = blockDim.x >> 6;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, nw = sm.nt >> 6;
   const uint8_t *m_row = r.mask + (int64_t)b * L;
   uint8_t *o_row = r.out + (int64_t)b * L;
   // the score is loaded whatever the mask says, so both loads are in flight
@@ -324,7 +326,7 @@ __device__ inline RuleCount short_rank_rule(const RuleDev &r, int b, int L, cons
     }
     return RuleCount{n, nc1};
   }
-  const int P = owners_for(n, blockDim.x);
+  const int P = owners_for(n, sm.nt);
   double unused;
   uint64_t q;
   const int rank = block_rank<false>(n, n, kSentinel, sm.keys, n, nullptr, sm, P, unused, q);
@@ -359,7 +361,7 @@ __device__ inline RuleCount short_rank_rule(const RuleDev &r, int b, int L, cons
 __device__ inline bool short_entropy_rule(const RuleDev &r, int b, int L, const float *ent,
                                           const RuleSmem &sm, const CommitSink &sk,
                                           RuleCount &rc) {
-  const int t = threadIdx.x, nt = blockDim.x, lane = t & 63, wave = t >> 6, nw = nt >> 6;
+  const int t = threadIdx.x, nt = sm.nt, lane = t & 63, wave = t >> 6, nw = nt >> 6;
   const uint8_t *m_row = r.mask + (int64_t)b * L;
   uint8_t *o_row = r.out + (int64_t)b * L;
   const float hv = t < L ? load_coherent(ent + (int64_t)b * L + t) : 0.f;   // with the mask
@@ -493,8 +495,8 @@ __device__ inline bool short_entropy_rule(const RuleDev &r, int b, int L, const 
 // ---------------------------------------------------------------- long rows
 
 // Plain LDS bitonic sort of Np keys, ascending.
-__device__ inline void block_sort_lds(uint64_t *keys, int Np) {
-  const int tid = threadIdx.x, nt = blockDim.x;
+__device__ inline void block_sort_lds(uint64_t *keys, int Np, int nt) {
+  const int tid = threadIdx.x;
   for (int k = 2; k <= Np; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
       for (int i = tid; i < (Np >> 1); i += nt) {
@@ -515,7 +517,7 @@ __device__ inline void block_sort_lds(uint64_t *keys, int Np) {
 // Sorted candidate keys of batch row b in sm.keys[0..nc); returns nc.
 __device__ inline int sort_candidates(const RuleDev &r, int b, int L, const float *score,
                                       bool by_entropy, const RuleSmem &sm) {
-  const int tid = threadIdx.x, nt = blockDim.x;
+  const int tid = threadIdx.x, nt = sm.nt;
   const int Np = rule_pow2(L);
   const float *s_row = score + (int64_t)b * L;
   const uint8_t *m_row = r.mask + (int64_t)b * L;
@@ -536,7 +538,7 @@ __device__ inline int sort_candidates(const RuleDev &r, int b, int L, const floa
   if (mine) atomicAdd(cnt, mine);
   __syncthreads();
   const int nc = *cnt;
-  block_sort_lds(sm.keys, Np);
+  block_sort_lds(sm.keys, Np, nt);
   return nc;
 }
 
@@ -545,12 +547,12 @@ __device__ inline RuleCount commit_sorted(const RuleDev &r, int b, int L, int n,
                                           const RuleSmem &sm, const CommitSink &sk) {
   uint8_t *o_row = r.out + (int64_t)b * L;
   const uint8_t *m_row = r.mask + (int64_t)b * L;
-  for (int i = threadIdx.x; i < nc; i += blockDim.x) {
+  for (int i = threadIdx.x; i < nc; i += sm.nt) {
     const uint32_t pos = (uint32_t)sm.keys[i];
     o_row[pos] = i < n ? 1 : 0;
     if (i < n && sk.canvas) sk.canvas[pos] = load_coherent_i32(sk.x0 + pos);
   }
-  for (int l = threadIdx.x; l < L; l += blockDim.x)
+  for (int l = threadIdx.x; l < L; l += sm.nt)
     if (!m_row[l]) o_row[l] = 0;
   return RuleCount{nc, n};
 }
@@ -566,7 +568,7 @@ __device__ inline RuleCount long_rank_rule(const RuleDev &r, int b, int L, const
     int *first_fail = sm.misc + 6;
     if (threadIdx.x == 0) *first_fail = nc;
     __syncthreads();
-    for (int i = threadIdx.x; i < nc; i += blockDim.x)
+    for (int i = threadIdx.x; i < nc; i += sm.nt)
       if (!factor_holds(i, conf_from_key((uint32_t)(sm.keys[i] >> 32)), r.param))
         atomicMin(first_fail, i);
     __syncthreads();
@@ -608,7 +610,7 @@ __device__ inline RuleCount long_entropy_rule(const RuleDev &r, int b, int L, co
 // threshold: no ranking needed.
 __device__ inline RuleCount rule_threshold(const RuleDev &r, int b, int L, const float *conf,
                                            const RuleSmem &sm, const CommitSink &sk) {
-  const int tid = threadIdx.x, nt = blockDim.x;
+  const int tid = threadIdx.x, nt = sm.nt;
   unsigned long long *best = reinterpret_cast<unsigned long long *>(sm.misc + 24);
   int *n_pass = sm.misc + 2;
   int *n_cand = sm.misc + 3;
@@ -655,9 +657,9 @@ __device__ inline RuleCount rule_threshold(const RuleDev &r, int b, int L, const
 // Returns the candidate and commit counts (valid in thread 0).
 __device__ inline RuleCount run_batch_rule(const RuleDev &r, int b, int L, const float *conf,
                                            const float *ent, unsigned char *smem,
-                                           const CommitSink &sk) {
-  const RuleSmem sm = rule_smem(smem, L);
-  const bool short_row = L <= (int)blockDim.x;
+                                           const CommitSink &sk, int nt) {
+  const RuleSmem sm = rule_smem(smem, L, nt);
+  const bool short_row = L <= nt;
   RuleCount rc{0, 0};
   switch (r.kind) {
     case DLLM_RULE_THRESHOLD:

@@ -767,7 +767,7 @@ __device__ inline void finish_counts(const StatsArgs &a, uint32_t b, int edits,
 // The batch row's statistics are all published: rank rules (the first one
 // also updating the canvas), then the counts.
 __device__ inline void complete_batch_row(const StatsArgs &a, uint32_t b, unsigned char *smem,
-                                          int edits) {
+                                          int edits, int nt) {
   RuleCount rc0{0, 0};
   for (int r = 0; r < a.n_rank_rules; ++r) {
     const RuleDev &rule = a.rank_rules[r];
@@ -776,7 +776,7 @@ __device__ inline void complete_batch_row(const StatsArgs &a, uint32_t b, unsign
                                                                : a.prob;
     const CommitSink sk{r == 0 && a.canvas ? a.canvas + (int64_t)b * a.L : nullptr,
                         a.x0 + (int64_t)b * a.L};
-    const RuleCount rc = run_batch_rule(rule, (int)b, (int)a.L, conf, a.entropy, smem, sk);
+    const RuleCount rc = run_batch_rule(rule, (int)b, (int)a.L, conf, a.entropy, smem, sk, nt);
     if (r == 0) rc0 = rc;
   }
   finish_counts(a, b, edits, rc0);
@@ -787,18 +787,19 @@ __device__ inline void complete_batch_row(const StatsArgs &a, uint32_t b, unsign
 // batch row; the workgroup that completes the batch row runs the rank rules on
 // the statistics the launch has just written (coherent loads), then the canvas
 // update and the counts.
-__device__ inline void finish_row(const StatsArgs &a, uint32_t b, unsigned char *smem) {
+__device__ inline void finish_row(const StatsArgs &a, uint32_t b, unsigned char *smem, int nt,
+                                  uint32_t *batch_cnt) {
   __shared__ int s_last;
   const int tid = threadIdx.x;
   if (!a.need_batch) return;
   if (tid == 0) {
     wait_stores_complete();
-    const uint32_t prev = atomicAdd(&a.batch_count[b], 1u);
+    const uint32_t prev = atomicAdd(batch_cnt, 1u);
     s_last = (prev == (uint32_t)(a.L - 1));
   }
   __syncthreads();
   if (!s_last) return;
-  complete_batch_row(a, b, smem, -1);
+  complete_batch_row(a, b, smem, -1, nt);
 }
 
 template <typename T, int NT, int UV, bool SAMPLE, bool VECLOAD, bool FULL>
@@ -824,7 +825,7 @@ __global__ __launch_bounds__(NT) void token_stats_kernel(StatsArgs a) {
   if (FULL && a.skip_rows && !row_needed(a, row_id)) {
     if (slice != 0) return;
     if (tid == 0 && a.has_edit) a.edit_out[row_id] = 0;
-    finish_row(a, b, smem);
+    finish_row(a, b, smem, NT, a.batch_count + b);
     return;
   }
 
@@ -841,6 +842,13 @@ __global__ __launch_bounds__(NT) void token_stats_kernel(StatsArgs a) {
   stream_slice<T, NT, UV, SAMPLE, VECLOAD, FULL>(a, row, lo, hi, b, l, wave_parts,
                                                  &slice_parts_acc);
 
+  // The hand-off counters' base addresses, loaded here (an empty asm that
+  // uses them) so that these argument loads are not on the hand-off's
+  // critical path once the stores have drained.
+  asm volatile("" ::"s"(a.row_count), "s"(a.batch_count));
+  uint32_t *row_cnt = a.row_count + row_id;    // used only with split rows
+  uint32_t *batch_cnt = a.batch_count + b;
+
   // Split rows: publish the slice partial and count it on the row's own
   // counter (a counter per row keeps the atomics of a launch spread out); the
   // last slice to arrive fetches every slice's partial at once into LDS and
@@ -850,7 +858,7 @@ __global__ __launch_bounds__(NT) void token_stats_kernel(StatsArgs a) {
     if (tid == 0) {
       store_partial(&parts[slice], slice_parts_acc);
       wait_stores_complete();
-      const uint32_t prev = atomicAdd(&a.row_count[row_id], 1u);
+      const uint32_t prev = atomicAdd(row_cnt, 1u);
       s_flag = (prev == (uint32_t)(a.slices - 1));
     }
     __syncthreads();
@@ -871,7 +879,7 @@ __global__ __launch_bounds__(NT) void token_stats_kernel(StatsArgs a) {
       acc = butterfly_merge<SAMPLE>(acc, n, a.c2);
       if (tid == 0) {
         slice_parts_acc = acc;
-        a.row_count[row_id] = 0u;
+        *row_cnt = 0u;
       }
     }
     __syncthreads();
@@ -894,7 +902,7 @@ __global__ __launch_bounds__(NT) void token_stats_kernel(StatsArgs a) {
       w[1] = make_uint4(0u, 0u, 0u, 0u);
     }
   }
-  finish_row(a, b, smem);
+  finish_row(a, b, smem, NT, batch_cnt);
 }
 
 // ---------------------------------------------------------------- launch plan
