@@ -107,6 +107,9 @@ def _run_and_check(arr, dtype, tokens, cand, editable, kind, param, strict=False
     ("factor", 1.0, False, "f32", 3, 40, 9000, 0.0),
     ("topk", 5, False, "bf16", 2, 100, 12000, 0.7),            # sampled x0
     ("threshold", 0.5, False, "bf16", 1, 600, 4096, 0.0),      # L > 512: sorted rule path
+    ("topk", 37, False, "bf16", 1, 700, 5000, 0.0),            # long rows: sorted commits + canvas
+    ("factor", 2.0, False, "f32", 2, 300, 3000, 0.0),
+    ("entropy_bound", 1.5, False, "bf16", 1, 700, 5000, 0.0),
 ])
 def test_commit_step_matches_oracle(kind, param, strict, dtype, B, L, V, T):
     rng = np.random.default_rng(31 + L)
