@@ -403,7 +403,8 @@ __device__ __forceinline__ bool is_suppressed(const StatsArgs &a, int64_t v) {
 
 __device__ __forceinline__ float gumbel_at(const StatsArgs &a, uint32_t b, uint32_t l, int64_t v) {
   const Philox4 p = philox4x32_10((uint32_t)(v >> 2), l, b, a.step, a.key0, a.key1);
-  return gumbel_from_word(p.w[v & 3]);
+  const int j = (int)(v & 3);       // a select, not an indexed load (no scratch)
+  return gumbel_from_word(j == 0 ? p.w[0] : j == 1 ? p.w[1] : j == 2 ? p.w[2] : p.w[3]);
 }
 
 // Stream [lo, hi) of one row.  VECLOAD: 16-byte loads (row start 16-byte
