@@ -18,15 +18,12 @@ HIPCC = "/opt/rocm/bin/hipcc"
 pytestmark = pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not installed")
 
 
-def _kernels(src, tmp_path):
-    from commit_step_amd.build import FLAGS
-    flags = [f for f in FLAGS if f not in ("-shared", "-fPIC")]
-    out = tmp_path / (os.path.basename(src) + ".s")
-    subprocess.run([HIPCC, *flags, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-                    "--cuda-device-only", "-S", "-o", str(out), os.path.join(CSRC, src)],
-                   check=True, capture_output=True)
+SOURCES = ["token_stats.hip", "token_stats_full.hip", "transfer.hip", "uniform.hip"]
+
+
+def _parse(path):
     found, cur = {}, None
-    for line in out.read_text().splitlines():       # the amdhsa metadata, one kernel at a time
+    for line in open(path).read().splitlines():     # the amdhsa metadata, one kernel at a time
         m = re.match(r"\s+\.name:\s+(_Z\S+)$", line)
         if m:
             cur = found.setdefault(m.group(1), {})
@@ -37,10 +34,30 @@ def _kernels(src, tmp_path):
     return found
 
 
-@pytest.mark.parametrize("src", ["token_stats.hip", "token_stats_full.hip", "transfer.hip",
-                                 "uniform.hip"])
-def test_no_scratch_and_vgpr_budget(src, tmp_path):
-    ks = _kernels(src, tmp_path)
+@pytest.fixture(scope="module")
+def kernels(tmp_path_factory):
+    """Every source compiled to gfx950 assembly, in parallel."""
+    from commit_step_amd.build import FLAGS
+    flags = [f for f in FLAGS if f not in ("-shared", "-fPIC")]
+    tmp = tmp_path_factory.mktemp("asm")
+    procs = {}
+    for src in SOURCES:
+        out = tmp / (src + ".s")
+        procs[src] = (out, subprocess.Popen(
+            [HIPCC, *flags, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+             "--cuda-device-only", "-S", "-o", str(out), os.path.join(CSRC, src)],
+            stdout=subprocess.PIPE, stderr=subprocess.STDOUT))
+    result = {}
+    for src, (out, pr) in procs.items():
+        pr.communicate()
+        assert pr.returncode == 0, f"hipcc -S failed for {src}"
+        result[src] = _parse(out)
+    return result
+
+
+@pytest.mark.parametrize("src", SOURCES)
+def test_no_scratch_and_vgpr_budget(src, kernels):
+    ks = kernels[src]
     assert ks, f"no kernels found in {src}"
     for name, r in ks.items():
         assert r["private_segment_fixed_size"] == 0, f"{name} uses scratch: {r}"
