@@ -167,12 +167,14 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
   return o;
 }
 
-// Gumbel(0,1) draw from one Philox word: u = ((w >> 9) + 0.5) * 2^-23 (exact in
-// float32), g = -ln(-ln u) with the hardware base-2 logarithm.
-__device__ __forceinline__ float gumbel_from_word(uint32_t w) {
+// Gumbel(0,1) draw from one Philox word, u = ((w >> 9) + 0.5) * 2^-23 (exact in
+// float32), in base-2 units: returns -log2(-log2 u), which is log2(e) g + log2(ln 2)
+// for the Gumbel draw g = -ln(-ln u).  With the logit scaled by log2(e) / T, the
+// score x log2(e) / T - log2(-log2 u) is log2(e) (x / T + g) plus a constant: the
+// same argmax as the Gumbel-max score, with two multiplies fewer per element.
+__device__ __forceinline__ float gumbel2_from_word(uint32_t w) {
   const float u = fmaf((float)(w >> 9), 0x1p-23f, 0x1p-24f);
-  const float a = -__builtin_amdgcn_logf(u);          // -log2 u > 0
-  return -kLn2 * __builtin_amdgcn_logf(a * kLn2);     // -ln(-ln u)
+  return -__builtin_amdgcn_logf(-__builtin_amdgcn_logf(u));   // -log2(-log2 u)
 }
 
 // ---------------------------------------------------------------- exact sums

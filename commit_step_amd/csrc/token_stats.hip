@@ -220,7 +220,7 @@ int stats_step(const char *who, const void *logits, int dtype, int64_t B, int64_
   a.L = L;
   a.slice_len = p.slice_len;
   a.slices = p.slices;
-  a.inv_temp = temperature > 0.0f ? 1.0f / temperature : 0.0f;
+  a.inv_temp = temperature > 0.0f ? (float)(1.4426950408889634 / (double)temperature) : 0.0f;
   a.key0 = (uint32_t)(seed & 0xffffffffu);
   a.key1 = (uint32_t)(seed >> 32);
   a.step = (uint32_t)step;

@@ -126,7 +126,7 @@ struct StatsArgs {
   int has_edit;
   int n_suppress;
   int first_allowed;       // lowest id not suppressed
-  float inv_temp;
+  float inv_temp;          // log2(e) / T: the Gumbel-max score in base-2 units
   uint32_t key0, key1, step;
   int32_t *x0;
   float *prob;
@@ -404,7 +404,7 @@ __device__ __forceinline__ bool is_suppressed(const StatsArgs &a, int64_t v) {
 __device__ __forceinline__ float gumbel_at(const StatsArgs &a, uint32_t b, uint32_t l, int64_t v) {
   const Philox4 p = philox4x32_10((uint32_t)(v >> 2), l, b, a.step, a.key0, a.key1);
   const int j = (int)(v & 3);       // a select, not an indexed load (no scratch)
-  return gumbel_from_word(j == 0 ? p.w[0] : j == 1 ? p.w[1] : j == 2 ? p.w[2] : p.w[3]);
+  return gumbel2_from_word(j == 0 ? p.w[0] : j == 1 ? p.w[1] : j == 2 ? p.w[2] : p.w[3]);
 }
 
 // Stream [lo, hi) of one row.  VECLOAD: 16-byte loads (row start 16-byte
@@ -469,7 +469,7 @@ __device__ void stream_slice(const StatsArgs &a, const T *row, int64_t lo, int64
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               const float xv = x[k * VEC + 4 * q + j];
-              const float sc = fmaf(xv, a.inv_temp, gumbel_from_word(p.w[j]));
+              const float sc = fmaf(xv, a.inv_temp, gumbel2_from_word(p.w[j]));
               if (sc > st.sb) { st.sb = sc; st.ib = (int)(vq + j); st.xb = xv; }
             }
           }
