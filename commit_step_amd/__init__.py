@@ -10,6 +10,7 @@ functions ("dLLM block decoding", "What mlx-arsenal ships"): token_stats,
 threshold_transfer, topk_transfer, factor_transfer, entropy_bound_transfer,
 edit_transfer, transfer_schedule, block_ranges, block_causal_mask.
 """
+import contextlib
 import ctypes
 import os
 from collections import namedtuple
@@ -118,7 +119,7 @@ def _stream(t):
 
 
 def _dev(t, name):
-    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise ValueError(f"{name} must be a CUDA (HIP) tensor")
     return t
 
@@ -129,9 +130,29 @@ def _bl(t, name, dtypes, shape=None):
         raise ValueError(f"{name} must have dtype in {dtypes}, not {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    if shape is not None and tuple(t.shape) != tuple(shape):
+    if shape is not None and t.shape != shape:
         raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
     return t
+
+
+def _on(device):
+    """The device's context, skipped when it is already the current device
+    (entering it costs more host time than the launch itself)."""
+    if device.index is None or device.index == torch.cuda.current_device():
+        return contextlib.nullcontext()
+    return torch.cuda.device(device)
+
+
+_ws_sizes = {}
+
+
+def _ws_size(dt, B, L, V, device):
+    key = (dt, B, L, V, device.index)
+    n = _ws_sizes.get(key)
+    if n is None:
+        n = int(load_library().dllm_token_stats_workspace_size(dt, B, L, V))
+        _ws_sizes[key] = n
+    return n
 
 
 _MASK_DTYPES = (torch.bool, torch.uint8)
@@ -141,7 +162,7 @@ _workspaces = {}
 def workspace_size(logits):
     B, L, V = logits.shape
     dt = DLLM_BF16 if logits.dtype == torch.bfloat16 else DLLM_F32
-    with torch.cuda.device(logits.device):
+    with _on(logits.device):
         return int(load_library().dllm_token_stats_workspace_size(dt, B, L, V))
 
 
@@ -337,8 +358,8 @@ def _stats_call(logits, temperature, seed, step, suppress_ids, rules, out, works
                 c.tokens = r.tokens.data_ptr()
     dt = DLLM_BF16 if logits.dtype == torch.bfloat16 else DLLM_F32
     lib = load_library()
-    with torch.cuda.device(dev):
-        need = int(lib.dllm_token_stats_workspace_size(dt, B, L, V))
+    with _on(dev):
+        need = _ws_size(dt, B, L, V, dev)
         ws = workspace if workspace is not None else _workspace(dev, need)
         args = [logits.data_ptr(), dt, B, L, V, row_stride, float(temperature),
                 int(seed or 0) & 0xFFFFFFFFFFFFFFFF, int(step), sup, len(suppress_ids),
@@ -369,12 +390,12 @@ def threshold_transfer(prob, candidates, threshold, strict=False, out=None):
     B, L = prob.shape
     if isinstance(threshold, torch.Tensor):
         taus = _bl(threshold, "threshold", (torch.float64,), (B,))
-        with torch.cuda.device(prob.device):
+        with _on(prob.device):
             _check(load_library().dllm_transfer_threshold_rows(
                 prob.data_ptr(), candidates.data_ptr(), taus.data_ptr(), B, L,
                 int(bool(strict)), out.data_ptr(), _stream(prob)), "dllm_transfer_threshold_rows")
         return out
-    with torch.cuda.device(prob.device):
+    with _on(prob.device):
         _check(load_library().dllm_transfer_threshold(
             prob.data_ptr(), candidates.data_ptr(), B, L, float(threshold), int(bool(strict)),
             out.data_ptr(), _stream(prob)), "dllm_transfer_threshold")
@@ -397,7 +418,7 @@ def topk_transfer(prob, candidates, k, out=None):
     out = _rule_out(prob, candidates, out)
     B, L = prob.shape
     kt = _k_tensor(k, B, prob.device)
-    with torch.cuda.device(prob.device):
+    with _on(prob.device):
         _check(load_library().dllm_transfer_topk(
             prob.data_ptr(), candidates.data_ptr(), kt.data_ptr(), B, L, out.data_ptr(),
             _stream(prob)), "dllm_transfer_topk")
@@ -409,7 +430,7 @@ def factor_transfer(prob, candidates, factor, out=None):
     _bl(prob, "prob", (torch.float32,))
     out = _rule_out(prob, candidates, out)
     B, L = prob.shape
-    with torch.cuda.device(prob.device):
+    with _on(prob.device):
         _check(load_library().dllm_transfer_factor(
             prob.data_ptr(), candidates.data_ptr(), B, L, float(factor), out.data_ptr(),
             _stream(prob)), "dllm_transfer_factor")
@@ -421,7 +442,7 @@ def entropy_bound_transfer(entropy, candidates, gamma, out=None):
     _bl(entropy, "entropy", (torch.float32,))
     out = _rule_out(entropy, candidates, out)
     B, L = entropy.shape
-    with torch.cuda.device(entropy.device):
+    with _on(entropy.device):
         _check(load_library().dllm_transfer_entropy_bound(
             entropy.data_ptr(), candidates.data_ptr(), B, L, float(gamma), out.data_ptr(),
             _stream(entropy)), "dllm_transfer_entropy_bound")
@@ -435,7 +456,7 @@ def edit_transfer(x0, prob, tokens, editable, editing_threshold, out=None):
     _bl(x0, "x0", (torch.int32,), (B, L))
     _bl(tokens, "tokens", (torch.int32,), (B, L))
     out = _rule_out(prob, editable, out)
-    with torch.cuda.device(prob.device):
+    with _on(prob.device):
         _check(load_library().dllm_transfer_edit(
             x0.data_ptr(), prob.data_ptr(), tokens.data_ptr(), editable.data_ptr(), B, L,
             float(editing_threshold), out.data_ptr(), _stream(prob)), "dllm_transfer_edit")
@@ -449,7 +470,7 @@ def transfer_schedule(n_masked, steps, out=None):
     if out is None:
         out = torch.empty((B, int(steps)), dtype=torch.int32, device=n_masked.device)
     _bl(out, "out", (torch.int32,), (B, int(steps)))
-    with torch.cuda.device(n_masked.device):
+    with _on(n_masked.device):
         _check(load_library().dllm_transfer_schedule(
             n_masked.data_ptr(), B, int(steps), out.data_ptr(), _stream(n_masked)),
             "dllm_transfer_schedule")
@@ -472,7 +493,7 @@ def block_causal_mask(L, block_len, device="cuda", out=None):
     if out is None:
         out = torch.empty((int(L), int(L)), dtype=torch.float32, device=device)
     _bl(out, "out", (torch.float32,), (int(L), int(L)))
-    with torch.cuda.device(out.device):
+    with _on(out.device):
         _check(load_library().dllm_block_causal_mask(int(L), int(block_len), out.data_ptr(),
                                                      _stream(out)), "dllm_block_causal_mask")
     return out
@@ -497,7 +518,7 @@ def uniform_canvas(shape, vocab_size, seed, draw, device=None, out=None):
     if out is None:
         out = torch.empty((B, L), dtype=torch.int32, device=dev)
     _bl(out, "out", (torch.int32,), (B, L))
-    with torch.cuda.device(out.device):
+    with _on(out.device):
         _check(load_library().dllm_uniform_canvas(out.data_ptr(), B, L, int(vocab_size),
                                                   int(seed) & 0xFFFFFFFFFFFFFFFF, int(draw),
                                                   _stream(out)), "dllm_uniform_canvas")
@@ -513,7 +534,7 @@ def renoise(sample, accepted, noise, out=None):
     if out is None:
         out = torch.empty_like(sample)
     _bl(out, "out", (torch.int32,), (B, L))
-    with torch.cuda.device(sample.device):
+    with _on(sample.device):
         _check(load_library().dllm_renoise(sample.data_ptr(), accepted.data_ptr(),
                                            noise.data_ptr(), B, L, out.data_ptr(),
                                            _stream(sample)), "dllm_renoise")
@@ -540,7 +561,7 @@ class StableConfidentStopping:
             self.prev = torch.empty((B, L), dtype=torch.int32, device=dev)
             self.count = torch.zeros((B,), dtype=torch.int32, device=dev)
             self.done = torch.zeros((B,), dtype=torch.uint8, device=dev)
-        with torch.cuda.device(argmax.device):
+        with _on(argmax.device):
             _check(load_library().dllm_stable_confident_stop(
                 argmax.data_ptr(), entropy.data_ptr(), B, L, self.k, self.c, int(first),
                 self.prev.data_ptr(), self.count.data_ptr(), self.done.data_ptr(),
