@@ -195,6 +195,9 @@ int stats_step(const char *who, const void *logits, int dtype, int64_t B, int64_
   a.need_batch = (a.n_rank_rules > 0 || a.counts) ? 1 : 0;
 
   const int64_t rows = B * L;
+  if (B > 0x7fffffffLL || L > 0x7fffffffLL || rows > (int64_t)(0xffffffffu / 1024u))
+    return fail(DLLM_ERR_UNSUPPORTED, "%s: B * L = %lld positions exceeds the launch limit of %u", who,
+                (long long)rows, 0xffffffffu / 1024u);
   const Plan p = make_plan(dtype, rows, V, row_stride, logits);
   const size_t need = workspace_bytes_for(B, L, p.slices);
   if (!workspace) return fail(DLLM_ERR_ARG, "%s: workspace is NULL", who);

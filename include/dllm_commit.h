@@ -32,6 +32,9 @@
  *  - A batch row may hold at most DLLM_MAX_L positions for the ranking rules
  *    (threshold, topk, factor, entropy_bound); longer rows return
  *    DLLM_ERR_UNSUPPORTED.
+ *  - dllm_token_stats / dllm_commit_step take at most (2^32 - 1) / 1024 = 4194303
+ *    positions B * L per call (one workgroup per position or slice of a
+ *    position); more return DLLM_ERR_UNSUPPORTED.
  */
 #ifndef DLLM_COMMIT_H
 #define DLLM_COMMIT_H

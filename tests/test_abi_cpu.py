@@ -108,6 +108,8 @@ def test_token_stats_argument_errors(lib):
     rules[0].kind, rules[0].score = dc.RULE_THRESHOLD, 0
     # empty shapes: OK with nothing launched
     assert call(B=0) == 0 and call(L=0) == 0
+    # more positions than one launch can hold
+    assert call(B=4096, L=1025) == -5 and "launch limit" in _err(lib)
 
 
 def test_commit_step_argument_errors(lib):
