@@ -193,6 +193,8 @@ static int launch_batch_rule(const dllm_rule &rule, int64_t B, int64_t L, const 
   // one position per thread (the short-row paths) up to 1024 positions
   const int np = rule_pow2((int)L);
   const int nt = np > 512 ? 1024 : (np > 256 ? 512 : 256);
+  if (B > (int64_t)(0xffffffffu / (unsigned)nt))
+    return fail(DLLM_ERR_UNSUPPORTED, "%s: B = %lld batch rows exceeds the launch limit", who, (long long)B);
   const size_t smem = rule_smem_bytes((int)L, nt);
   if (nt == 1024)
     batch_rule_kernel<1024><<<dim3((unsigned)B), dim3(1024), smem, s>>>(d, (int)L, scores, scores);
@@ -333,7 +335,7 @@ extern "C" int dllm_block_causal_mask(int64_t L, int64_t block_len, float *out, 
   if (L < 0 || block_len < 1) return fail(DLLM_ERR_ARG, "%s: need L >= 0 and block_len >= 1", who);
   if (L == 0) return ok();
   if (!out) return fail(DLLM_ERR_ARG, "%s: out is NULL", who);
-  if (L > 0x7fffffffLL) return fail(DLLM_ERR_UNSUPPORTED, "%s: L too large", who);
+  if (L > (int64_t)(0xffffffffu / 256u)) return fail(DLLM_ERR_UNSUPPORTED, "%s: L too large", who);
   const int vec_ok = (L % 4 == 0) && ((uintptr_t)out % 16 == 0);
   block_mask_kernel<<<dim3((unsigned)L), dim3(256), 0, stream>>>(L, block_len, out, vec_ok);
   return check_launch(who);

@@ -182,7 +182,8 @@ extern "C" int dllm_stable_confident_stop(const int32_t *argmax, const float *en
                                           uint8_t *done, hipStream_t stream) {
   const char *who = "dllm_stable_confident_stop";
   if (B < 0 || L < 0) return fail(DLLM_ERR_ARG, "%s: B and L must be >= 0", who);
-  if (B > 0x7fffffffLL || L > 0xffffffffLL) return fail(DLLM_ERR_UNSUPPORTED, "%s: B or L too large", who);
+  if (B > (int64_t)(0xffffffffu / 256u) || L > 0xffffffffLL)
+    return fail(DLLM_ERR_UNSUPPORTED, "%s: B or L too large", who);
   if (stability_threshold < 0) return fail(DLLM_ERR_ARG, "%s: stability_threshold < 0", who);
   if (confidence_threshold != confidence_threshold)
     return fail(DLLM_ERR_ARG, "%s: confidence_threshold is NaN", who);
