@@ -310,11 +310,20 @@ __device__ inline RuleCount short_rank_rule(const RuleDev &r, int b, int L, cons
     const uint64_t qk = own ? sm.keys[lane] : kSentinel;
     int rk = 0;
     double unused1;
-    if (own) count_below<false>(qk, sm.keys, nullptr, 0, n, rk, unused1);
     int nc1;
     if (r.kind == DLLM_RULE_TOPK) {
       nc1 = kq < 0 ? 0 : (kq > n ? n : kq);
+      // a quota of none, all or one needs no all-pairs ranks: the single
+      // commit of a quota of one is the smallest key (the most confident)
+      if (nc1 == 1) {
+        const uint64_t best = wave_min_u64(qk);      // every lane takes part in the reduction
+        rk = (own && qk == best) ? 0 : 1;
+      }
+      else if (nc1 == 0 || nc1 == n) rk = 0;
+      else if (own) count_below<false>(qk, sm.keys, nullptr, 0, n, rk, unused1);
+      if (nc1 == 0) rk = 1;
     } else {
+      if (own) count_below<false>(qk, sm.keys, nullptr, 0, n, rk, unused1);
       const bool fails = own && !factor_holds(rk, conf_from_key((uint32_t)(qk >> 32)), r.param);
       const int first = wave_min_i(fails ? rk : 0x7fffffff);
       nc1 = n ? max(first < n ? first : n, 1) : 0;
