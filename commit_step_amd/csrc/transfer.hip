@@ -128,6 +128,41 @@ __global__ __launch_bounds__(NT) void batch_rule_kernel(RuleDev r, int L, const 
   run_batch_rule(r, (int)blockIdx.x, L, conf, ent, smem, CommitSink{nullptr, nullptr}, NT);
 }
 
+// The standalone threshold rule: one wave per batch row, four rows per
+// workgroup.  It needs no ranking, so the pass count and the forced first
+// maximal candidate are wave reductions; no LDS and no barrier.  Same decision
+// as the fused routine (rule_threshold).
+__global__ __launch_bounds__(256) void threshold_rows_kernel(RuleDev r, int64_t B, int L,
+                                                            const float *conf) {
+  const int lane = threadIdx.x & 63;
+  const int64_t b = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (b >= B) return;                           // whole waves only
+  const float *c_row = conf + b * L;
+  const uint8_t *m_row = r.mask + b * L;
+  uint8_t *o_row = r.out + b * L;
+  const double tau = r.taus ? r.taus[b] : r.param;
+  int pass = 0;
+  uint64_t best = kSentinel;
+#pragma unroll 4
+  for (int l = lane; l < L; l += 64) {
+    const float cv = c_row[l];
+    const uint8_t m = m_row[l];
+    uint8_t v = 0;
+    if (m) {
+      const float c = conf_sanitized(r.negate ? -cv : cv);
+      const double cd = (double)c;
+      v = (r.strict ? (cd > tau) : (cd >= tau)) ? 1 : 0;
+      pass += v;
+      const uint64_t key = ((uint64_t)conf_key(c) << 32) | (uint32_t)l;
+      best = key < best ? key : best;
+    }
+    o_row[l] = v;
+  }
+  pass = wave_sum_i(pass);
+  best = wave_min_u64(best);
+  if (lane == 0 && pass == 0 && best != kSentinel) o_row[(uint32_t)best] = 1;
+}
+
 __global__ void edit_kernel(const int32_t *x0, const float *prob, const int32_t *tokens,
                             const uint8_t *editable, int64_t n, double tau, uint8_t *edit) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
@@ -190,6 +225,12 @@ static int launch_batch_rule(const dllm_rule &rule, int64_t B, int64_t L, const 
   if (rc != DLLM_OK) return rc;
   if ((const void *)rule.out == (const void *)scores || (const void *)rule.out == (const void *)rule.mask)
     return fail(DLLM_ERR_ARG, "%s: the output aliases an input", who);
+  if (d.kind == DLLM_RULE_THRESHOLD) {
+    if (B > (int64_t)(0xffffffffu / 64u))
+      return fail(DLLM_ERR_UNSUPPORTED, "%s: B = %lld batch rows exceeds the launch limit", who, (long long)B);
+    threshold_rows_kernel<<<dim3((unsigned)((B + 3) / 4)), dim3(256), 0, s>>>(d, B, (int)L, scores);
+    return check_launch(who);
+  }
   // one position per thread (the short-row paths) up to 1024 positions
   const int np = rule_pow2((int)L);
   const int nt = np > 512 ? 1024 : (np > 256 ? 512 : 256);

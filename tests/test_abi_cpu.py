@@ -210,7 +210,8 @@ def test_transfer_argument_errors(lib):
     assert lib.dllm_transfer_schedule(fake, 1, 0, fake, None) == -1
     assert lib.dllm_block_causal_mask(8, 0, fake, None) == -1
     assert lib.dllm_block_causal_mask(1 << 25, 32, fake, None) == -5      # beyond the launch limit
-    assert lib.dllm_transfer_threshold(fake, fake, 1 << 23, 4096, 0.5, 0, ctypes.c_void_p(32), None) == -5
+    assert lib.dllm_transfer_factor(fake, fake, 1 << 23, 4096, 1.0, ctypes.c_void_p(32), None) == -5
+    assert lib.dllm_transfer_threshold(fake, fake, 1 << 27, 4, 0.5, 0, ctypes.c_void_p(32), None) == -5
     assert lib.dllm_block_ranges(0, 8, 0, 0, None, 0) == -1
     assert lib.dllm_block_ranges(-1, 8, 4, 0, None, 0) == -1
     for fn, args in [(lib.dllm_transfer_threshold, (fake, fake, 0, 4, 0.5, 0, fake, None)),
