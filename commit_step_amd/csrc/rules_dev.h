@@ -237,6 +237,66 @@ template <bool VALS>
 __device__ inline int block_rank(int nq, int n0, uint64_t extra, const uint64_t *list, int n,
                                  const double *vals, const RuleSmem &sm, int P, double &sum,
                                  uint64_t &query) {
+  if (nq <= 256) {
+    // Transposed: each wave scans a 1/nw share of the list for up to four
+    // queries per lane (query lane + 64 q), so every key read serves four
+    // comparisons.  The per-wave counts and sums meet in LDS atomics on
+    // part_cnt / part_sum, which the caller zeroed before its compaction
+    // barrier.  Counts are exact; the float64 sums then add in any order,
+    // which the callers' error bound already allows for.
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6, nw = sm.nt >> 6;
+    const int per = (n + nw - 1) / nw;
+    const int j0 = min(wave * per, n), j1 = min(j0 + per, n);
+    uint64_t qk[4];
+    int c[4];
+    double sq[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = lane + 64 * u;
+      qk[u] = i < n0 ? list[i] : (i < nq ? extra : 0ull);   // 0: no key lies below
+      c[u] = 0;
+      sq[u] = 0.0;
+    }
+    int j = j0;
+    for (; j + 4 <= j1; j += 4) {
+      uint64_t k[4];
+      double v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        k[e] = list[j + e];
+        if constexpr (VALS) v[e] = vals[j + e];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool lt = k[e] < qk[u];
+          c[u] += (int)lt;
+          if constexpr (VALS) sq[u] += lt ? v[e] : 0.0;
+        }
+    }
+    for (; j < j1; ++j) {
+      const uint64_t k = list[j];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool lt = k < qk[u];
+        c[u] += (int)lt;
+        if constexpr (VALS) sq[u] += lt ? vals[j] : 0.0;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = lane + 64 * u;
+      if (i < nq) {
+        if (c[u]) atomicAdd(&sm.part_cnt[i], c[u]);
+        if (VALS && sq[u] != 0.0) atomicAdd(&sm.part_sum[i], sq[u]);
+      }
+    }
+    __syncthreads();
+    query = t < n0 ? list[t] : (t < nq ? extra : kSentinel);
+    sum = (VALS && t < nq) ? sm.part_sum[t] : 0.0;
+    return t < nq ? sm.part_cnt[t] : 0;
+  }
   const int t = threadIdx.x, G = sm.nt / P, part = t / P, i = t - part * P;
   const int per = (n + G - 1) / G;
   const int j0 = min(part * per, n), j1 = min(j0 + per, n);
@@ -294,6 +354,7 @@ __device__ inline RuleCount short_rank_rule(const RuleDev &r, int b, int L, cons
   const float c = cand ? conf_sanitized(cv) : 0.f;
   const uint64_t key = cand ? (((uint64_t)conf_key(c) << 32) | (uint32_t)t) : kSentinel;
   int *wcnt = sm.misc, *wfail = sm.misc + 32;
+  sm.part_cnt[t] = 0;                         // for the transposed ranks
   const uint64_t m = __builtin_amdgcn_ballot_w64(cand);
   if (lane == 0) wcnt[wave] = __builtin_popcountll(m);
   __syncthreads();
@@ -385,6 +446,8 @@ __device__ inline bool short_entropy_rule(const RuleDev &r, int b, int L, const 
   int *wF = sm.misc, *wA = sm.misc + 16, *wFail = sm.misc + 32, *wUnc = sm.misc + 48;
   uint64_t *wNext = reinterpret_cast<uint64_t *>(sm.misc + 64);
   int *slot = sm.misc + 100;
+  sm.part_cnt[t] = 0;                         // for the transposed ranks
+  sm.part_sum[t] = 0.0;
   const uint64_t mF = __builtin_amdgcn_ballot_w64(in_f);
   const uint64_t mA = __builtin_amdgcn_ballot_w64(above);
   const bool wbad = __builtin_amdgcn_ballot_w64(bad) != 0;
