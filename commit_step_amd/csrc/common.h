@@ -152,12 +152,13 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
                                                  uint32_t c3, uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    // each 32 x 32 -> 64-bit product in one instruction (both halves at once)
+    // each 32 x 32 -> 64-bit product in one instruction (both halves at once),
+    // each three-way xor in one v_bitop3_b32 (truth table 0x96: odd parity)
     const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
     const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
-    c0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    c0 = __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x96);
     c1 = (uint32_t)p1;
-    c2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c2 = __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x96);
     c3 = (uint32_t)p0;
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
@@ -172,8 +173,11 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
 // for the Gumbel draw g = -ln(-ln u).  With the logit scaled by log2(e) / T, the
 // score x log2(e) / T - log2(-log2 u) is log2(e) (x / T + g) plus a constant: the
 // same argmax as the Gumbel-max score, with two multiplies fewer per element.
+// u is built without a conversion: one funnel shift puts the 23 word bits under
+// the exponent of 1.0 (the float 1 + m 2^-23, m = w >> 9), and subtracting
+// 1 - 2^-24 leaves (2m + 1) 2^-24, a 24-bit significand, so the difference is exact.
 __device__ __forceinline__ float gumbel2_from_word(uint32_t w) {
-  const float u = fmaf((float)(w >> 9), 0x1p-23f, 0x1p-24f);
+  const float u = __uint_as_float(__builtin_amdgcn_alignbit(0x7fu, w, 9)) - 0x1.fffffep-1f;
   return -__builtin_amdgcn_logf(-__builtin_amdgcn_logf(u));   // -log2(-log2 u)
 }
 
