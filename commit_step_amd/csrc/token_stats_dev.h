@@ -407,6 +407,43 @@ __device__ __forceinline__ float gumbel_at(const StatsArgs &a, uint32_t b, uint3
   return gumbel2_from_word(j == 0 ? p.w[0] : j == 1 ? p.w[1] : j == 2 ? p.w[2] : p.w[3]);
 }
 
+// The group of four whose best score the lane kept (st.ib its first index):
+// reload its logits (the sweep read them in whole 16-byte loads, so all four
+// lie in the row), suppress as the sweep did, rescore with the same operations
+// (the same bits), and keep the first element that reaches the group's best.
+template <typename T>
+__device__ __forceinline__ void recover_group_best(const StatsArgs &a, const T *row, uint32_t b,
+                                                   uint32_t l, WaveState &st) {
+  if (st.ib == kIdxNone) return;
+  const int vq = st.ib;
+  float xr[4];
+  if constexpr (sizeof(T) == 2) {
+    const uint2 w = *reinterpret_cast<const uint2 *>(row + vq);
+    xr[0] = __uint_as_float(w.x << 16); xr[1] = __uint_as_float(w.x & 0xffff0000u);
+    xr[2] = __uint_as_float(w.y << 16); xr[3] = __uint_as_float(w.y & 0xffff0000u);
+  } else {
+    const uint4 w = *reinterpret_cast<const uint4 *>(row + vq);
+    xr[0] = __uint_as_float(w.x); xr[1] = __uint_as_float(w.y);
+    xr[2] = __uint_as_float(w.z); xr[3] = __uint_as_float(w.w);
+  }
+  for (int i = 0; i < a.n_suppress; ++i) {
+    const int d = a.suppress[i] - vq;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (d == j) xr[j] = -kInf;
+  }
+  const Philox4 p = philox4x32_10((uint32_t)vq >> 2, l, b, a.step, a.key0, a.key1);
+  int jb = 0;
+  float xb = xr[0];
+#pragma unroll
+  for (int j = 3; j >= 0; --j) {
+    const float sc = fmaf(xr[j], a.inv_temp, gumbel2_from_word(p.w[j]));
+    if (sc == st.sb) { jb = j; xb = xr[j]; }
+  }
+  st.ib = vq + jb;
+  st.xb = xb;
+}
+
 // Stream [lo, hi) of one row.  VECLOAD: 16-byte loads (row start 16-byte
 // aligned, lo/hi multiples of VEC).  Full workgroup iterations run without
 // bounds checks, with the next iteration's loads in flight while the current
@@ -462,16 +499,20 @@ __device__ void stream_slice(const StatsArgs &a, const T *row, int64_t lo, int64
       for (int k = 0; k < U; ++k) {
         const int64_t v0 = base + (int64_t)(k * NT + tid) * VEC;
         if constexpr (VEC >= 4) {
+          // One generator call scores a group of four: only the group's best
+          // score and the group's first index are kept (strictly greater
+          // keeps the earlier group on ties); the element and its logit are
+          // recovered once, when the stream ends (recover_group_best).
 #pragma unroll
           for (int q = 0; q < VEC / 4; ++q) {
             const int64_t vq = v0 + 4 * q;
             const Philox4 p = philox4x32_10((uint32_t)(vq >> 2), l, b, a.step, a.key0, a.key1);
+            float sc[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const float xv = x[k * VEC + 4 * q + j];
-              const float sc = fmaf(xv, a.inv_temp, gumbel2_from_word(p.w[j]));
-              if (sc > st.sb) { st.sb = sc; st.ib = (int)(vq + j); st.xb = xv; }
-            }
+            for (int j = 0; j < 4; ++j)
+              sc[j] = fmaf(x[k * VEC + 4 * q + j], a.inv_temp, gumbel2_from_word(p.w[j]));
+            const float gm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+            if (gm > st.sb) { st.sb = gm; st.ib = (int)vq; }
           }
         } else {
           const float xv = x[k];
@@ -557,6 +598,8 @@ __device__ void stream_slice(const StatsArgs &a, const T *row, int64_t lo, int64
       process(x, base);
     }
   }
+
+  if constexpr (SAMPLE && VECLOAD) recover_group_best(a, row, b, l, st);
 
   // Wave partial -> LDS.
   Partial p;

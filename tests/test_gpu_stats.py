@@ -246,6 +246,29 @@ def test_suppressed_argmax_and_many_ids():
     assert not np.isin(gpu[0], sup).any()
 
 
+def test_sampled_suppressed_id_in_the_winning_group():
+    """Gumbel-max with a suppressed id of huge raw logit next to the token that
+    should win: the sampled pick shares its group of four generator words with
+    the suppressed id, and must still skip it."""
+    rng = np.random.default_rng(6)
+    B, L, V = 1, 12, 40000
+    x = (rng.standard_normal((B, L, V)) * 2).astype(np.float32)
+    sup = tuple(1000 + 5 * l for l in range(L))              # every slot of a group of four
+    for l in range(L):
+        s0 = sup[l]
+        x[0, l, s0] += 40.0                                   # suppressed raw argmax
+        x[0, l, (s0 & ~3) + ((s0 + 1) & 3)] += 25.0           # the winner, same group
+    bits = bf16_bits(x)
+    for T in (0.7, 1.0):
+        gpu = stats_np(dc.token_stats(to_dev(bits, "bf16"), temperature=T, seed=11, step=2,
+                                      suppress_ids=sup))
+        ref = oracle.token_stats(bits, "bf16", temperature=T, seed=11, step=2, suppress_ids=sup)
+        pos = [(0, l) for l in range(L)]
+        assert_sampled_x0(gpu[0], ref.x0, bits, "bf16", T, 11, 2, sup, pos, "sampled suppress")
+        assert not np.isin(gpu[0], sup).any()
+        assert_stats(gpu, ref, "bf16", "sampled suppress stats", mask=(gpu[0] == ref.x0))
+
+
 @pytest.mark.parametrize("dtype,B,L,V,T,seed,step", [
     ("bf16", 2, 16, 8192, 0.7, 1003, 0),
     ("bf16", 1, 8, 151936, 0.7, 1003, 3),
