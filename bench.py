@@ -307,13 +307,69 @@ def fused_workload(args):
     ms = start.elapsed_time(end) / steps
     logit_bytes = B * L * V * esz
     gbs = logit_bytes / (ms * 1e-3) / 1e9
-    print(json.dumps({
+    line = {
         "metric": "logit GB/s of the fused token_stats + rule launch", "value": round(gbs, 2),
         "unit": "GB/s", "n_gpus": 1, "steps": steps, "us_per_launch": round(ms * 1e3, 3),
         "higher_is_better": True, "dtype": "bf16" if esz == 2 else "f32", "data": "synthetic",
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "positions_per_s": round(B * L / (ms * 1e-3), 1),
-        "config": {"workload": label, "B": B, "L": L, "V": V, "copies": len(copies)}}), flush=True)
+        "config": {"workload": label, "B": B, "L": L, "V": V, "copies": len(copies)}}
+    if args.workload == "batched":
+        line["separate_calls"] = batched_separate_calls(dc, p, prob, cand, out, B, L)
+    print(json.dumps(line), flush=True)
+
+
+def batched_separate_calls(dc, p, prob, cand, out, B, L):
+    """The batched workload's separate calls, each timed alone (device calls as
+    graph replays): the standalone threshold over the fused launch's
+    probabilities, transfer_schedule, block_ranges (host) and the (2048, 2048)
+    additive block-causal mask."""
+    import torch
+
+    def timed(fn, n=50, reps=10):
+        # n launches captured in one HIP graph, so that the binding's host cost
+        # (several microseconds a call) is not what is timed
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(n):
+                fn()
+        g.replay()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / (n * reps) * 1e3
+
+    res = {}
+    us = timed(lambda: dc.threshold_transfer(prob, cand, p["tau"], strict=p["strict"], out=out))
+    moved = B * L * (4 + 1 + 1)                  # conf read, candidates read, commit written
+    res["threshold_transfer"] = {"B": B, "L": L, "us": round(us, 3),
+                                 "gb_s": round(moved / (us * 1e-6) / 1e9, 1)}
+    n_masked = torch.full((B,), L, dtype=torch.int32, device=prob.device)
+    sched = torch.empty((B, L), dtype=torch.int32, device=prob.device)
+    us = timed(lambda: dc.transfer_schedule(n_masked, L, out=sched))
+    res["transfer_schedule"] = {"B": B, "steps": L, "us": round(us, 3)}
+    t0 = time.perf_counter()
+    for _ in range(1000):
+        ranges = dc.block_ranges(p["prompt_len"], p["gen_len"], p["block_len"], align=True)
+    res["block_ranges"] = {"prompt_len": p["prompt_len"], "gen_len": p["gen_len"],
+                           "block_len": p["block_len"], "n_ranges": len(ranges),
+                           "host_us": round((time.perf_counter() - t0) * 1e3, 3)}
+    ML = p["mask_L"]
+    mask = torch.empty((ML, ML), dtype=torch.float32, device=prob.device)
+    us = timed(lambda: dc.block_causal_mask(ML, p["block_len"], out=mask))
+    gbs = ML * ML * 4 / (us * 1e-6) / 1e9
+    res["block_causal_mask"] = {"L": ML, "block_len": p["block_len"], "us": round(us, 3),
+                                "write_gb_s": round(gbs, 1),
+                                "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2)}
+    return res
 
 
 def main():
