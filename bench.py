@@ -483,9 +483,43 @@ def main():
                      "algorithmic_bytes_per_launch": alg_bytes},
         "kernel_source_sha256": src_hash,
     }
+    line["read_ceiling"] = read_ceiling(lib, rot, logit_bytes, B * L, args, ms, stream)
     line["cpu_baseline"] = None if args.no_cpu_baseline else \
         cpu_baseline(w, logit_bytes, args.cpu_seconds)
     print(json.dumps(line), flush=True)
+
+
+def read_ceiling(lib, rot, logit_bytes, rows, args, ms, stream):
+    """A plain read of the same rotated logit copies (dllm_read_probe, the same
+    16-byte loads, no arithmetic), timed like the step: once with the step's
+    decomposition (one row per 512-thread workgroup) and once over 8 x 256
+    workgroups of 256 threads; the step's time as a fraction of the faster."""
+    import torch
+
+    sink = torch.zeros(1, dtype=torch.int32, device=rot.device)
+    res = {}
+    for name, wgs, nt in (("row_per_workgroup", rows, 512), ("grid_2048x256", 2048, 256)):
+        args_i = [(rot[i].data_ptr(), logit_bytes, wgs, nt, sink.data_ptr(), stream)
+                  for i in range(rot.shape[0])]
+        rc = 0
+        for i in range(20):
+            rc |= lib.dllm_read_probe(*args_i[i % len(args_i)])
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(args.steps):
+            rc |= lib.dllm_read_probe(*args_i[i % len(args_i)])
+        b.record()
+        torch.cuda.synchronize()
+        if rc:
+            raise RuntimeError(lib.dllm_last_error().decode())
+        us = a.elapsed_time(b) / args.steps * 1e3
+        res[name] = {"workgroups": wgs, "threads": nt, "us": round(us, 3),
+                     "gb_s": round(logit_bytes / (us * 1e-6) / 1e9, 1)}
+    best = min(v["us"] for v in res.values())
+    res["step_time_over_best_read"] = round(ms * 1e3 / best, 3)
+    return res
 
 
 if __name__ == "__main__":

@@ -84,6 +84,7 @@ _SIGNATURES = {
     "dllm_renoise": (_I32, [_P, _P, _P, _I64, _I64, _P, _P]),
     "dllm_stable_confident_stop": (_I32, [_P, _P, _I64, _I64, _I32, ctypes.c_double, _I32, _P, _P,
                                           _P, _P]),
+    "dllm_read_probe": (_I32, [_P, _I64, _I64, _I32, _P, _P]),
     "dllm_last_error": (ctypes.c_char_p, []),
 }
 

@@ -9,7 +9,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SOURCES = ["csrc/token_stats.hip", "csrc/token_stats_full.hip", "csrc/transfer.hip",
-           "csrc/uniform.hip"]
+           "csrc/uniform.hip", "csrc/read_probe.hip"]
 LIB = os.path.join(HERE, "libdllm_commit.so")
 
 FLAGS = [

@@ -371,6 +371,17 @@ int dllm_stable_confident_stop(const int32_t *argmax, const float *entropy,
                                int32_t *prev_argmax, int32_t *stable_steps,
                                uint8_t *done, hipStream_t stream);
 
+/* Measurement helper, not a step of the commit: a plain streaming read of
+ * `bytes` bytes at `buf` (DEVICE, 16-byte aligned, bytes a positive multiple
+ * of 16) with the logit pass's 16-byte non-temporal loads, workgroup g reading
+ * the g-th of `workgroups` equal contiguous chunks with `threads` (256 or 512)
+ * threads.  It writes nothing but, in the rare case that a lane's xor of the
+ * words it read equals 0x9E3779B9, sets bit 0 of *sink (DEVICE uint32).
+ * Timing it over the logit buffers gives the read ceiling the logit pass is
+ * compared with. */
+int dllm_read_probe(const void *buf, int64_t bytes, int64_t workgroups, int threads,
+                    uint32_t *sink, hipStream_t stream);
+
 /* Message describing the last error returned on the calling thread ("" if
  * none). */
 const char *dllm_last_error(void);

@@ -167,6 +167,19 @@ def test_uniform_helpers_argument_errors(lib):
     assert stop(fake, P(24), 0, 3, 1, 0.1, 1, P(32), P(40), P(48), None) == 0
 
 
+def test_read_probe_argument_errors(lib):
+    P = ctypes.c_void_p
+    probe = lib.dllm_read_probe
+    assert probe(None, 64, 1, 256, P(64), None) == -1
+    assert probe(P(16), 64, 1, 256, None, None) == -1
+    assert probe(P(8), 64, 1, 256, P(64), None) == -1 and "aligned" in _err(lib)
+    assert probe(P(16), 60, 1, 256, P(64), None) == -1
+    assert probe(P(16), 0, 1, 256, P(64), None) == -1
+    assert probe(P(16), 64, 0, 256, P(64), None) == -1 and "workgroups" in _err(lib)
+    assert probe(P(16), 64, 1 << 31, 256, P(64), None) == -1
+    assert probe(P(16), 64, 1, 128, P(64), None) == -1 and "threads" in _err(lib)
+
+
 def test_decaying_threshold_host_parity(lib):
     import commit_step_amd as dc
     for t0, fl, d in product([0.95, 0.9, 1.0, 0.5], [0.95, 0.7, 0.0, -1.0], [0.0, 0.01, 0.05, 1e-9]):

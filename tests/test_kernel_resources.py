@@ -18,7 +18,8 @@ HIPCC = "/opt/rocm/bin/hipcc"
 pytestmark = pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not installed")
 
 
-SOURCES = ["token_stats.hip", "token_stats_full.hip", "transfer.hip", "uniform.hip"]
+SOURCES = ["token_stats.hip", "token_stats_full.hip", "transfer.hip", "uniform.hip",
+           "read_probe.hip"]
 
 
 def _parse(path):
