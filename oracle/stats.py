@@ -107,10 +107,9 @@ def token_stats_row(ell, temperature, seed, step, b, l, suppressed, stats_temper
         keep = allowed & (p > 0.0)
         H = -np.sum(p[keep] * ((ls[keep] - m) - log_z))
         # runner-up: the largest logit at any allowed index but the top one
-        r = -np.inf
-        for v in np.flatnonzero(allowed):
-            if v != top and ls[v] > r:
-                r = ls[v]
+        others = allowed.copy()
+        others[top] = False
+        r = ls[others].max() if others.any() else -np.inf
         margin = -np.expm1(r - m) / z                    # (1 - e^(r - m)) / z
         if sampling:
             with np.errstate(invalid="ignore"):

@@ -51,7 +51,7 @@ MUTATIONS = [
     ("rules.py", "start = (P // bl) * bl if align else P", "start = P", "block_ranges"),
     ("rules.py", "and _conf(prob[b, l]) > tau_edit", "and _conf(prob[b, l]) >= tau_edit",
      "edit"),
-    ("stats.py", "if v != top and ls[v] > r:", "if ls[v] > r:", "margin"),
+    ("stats.py", "others[top] = False", "others[top] = allowed[top]", "margin"),
     ("stats.py", "margin = -np.expm1(r - m) / z", "margin = (1.0 - np.exp(r - m)) / z", "margin"),
     ("stats.py", "(1.0 if n == 1 else 0.0)", "0.0", "margin"),
     ("stats.py", "ls = lp / stats_temperature", "ls = lp", "stats_temperature"),
