@@ -444,6 +444,16 @@ __device__ __forceinline__ void recover_group_best(const StatsArgs &a, const T *
   st.xb = xb;
 }
 
+// The greedy pass reads the output pointers (x0, prob, entropy, ...: one
+// line of the argument block) first when it publishes the row; loading one of
+// them while the first logit loads are in flight puts that line in the scalar
+// cache, so publication does not wait on the miss.  The sampled pass reads the
+// same line for its generator key at the start.
+template <bool SAMPLE>
+__device__ __forceinline__ void touch_publish_args(const StatsArgs &a) {
+  if constexpr (!SAMPLE) asm volatile("" ::"s"(a.x0));
+}
+
 // Stream [lo, hi) of one row.  VECLOAD: 16-byte loads (row start 16-byte
 // aligned, lo/hi multiples of VEC).  Full workgroup iterations run without
 // bounds checks, with the next iteration's loads in flight while the current
@@ -557,6 +567,7 @@ __device__ void stream_slice(const StatsArgs &a, const T *row, int64_t lo, int64
     if (n_full > 0) {
       uint4 ba[U], bb[U];
       load(ba, 0);
+      touch_publish_args<SAMPLE>(a);
       int64_t it = 0;
       for (; it + 2 < n_full; it += 2) {
         load(bb, it + 1);
@@ -586,6 +597,7 @@ __device__ void stream_slice(const StatsArgs &a, const T *row, int64_t lo, int64
           for (int e = 0; e < VEC; ++e) x[k * VEC + e] = -kInf;
         }
       }
+      touch_publish_args<SAMPLE>(a);
       process(x, tb);
     }
   } else {
