@@ -585,19 +585,29 @@ __device__ void stream_slice(const StatsArgs &a, const T *row, int64_t lo, int64
     }
     const int64_t tb = lo + n_full * STEP;
     if (tb < hi) {
+      // The masked iteration issues all its loads before it uses any (a load
+      // inside a divergent branch made the compiler wait for it there, one
+      // round trip per slot): a slot that no lane needs is skipped on a
+      // uniform branch, and a lane past the end reads the slice's first word
+      // instead (in bounds, its value unused).
+      uint4 r[U];
 #pragma unroll
       for (int k = 0; k < U; ++k) {
-        const int64_t v0 = tb + (int64_t)(k * NT + tid) * VEC;
-        if (v0 < hi) {
-          const uint4 r = load_stream(reinterpret_cast<const uint4 *>(row + v0));
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) x[k * VEC + e] = E::at(r, e);
-        } else {
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) x[k * VEC + e] = -kInf;
+        // a skipped slot keeps an unspecified value (an empty asm defines it
+        // without an instruction); no lane reads it
+        asm("" : "=v"(r[k].x), "=v"(r[k].y), "=v"(r[k].z), "=v"(r[k].w));
+        if (tb + (int64_t)k * NT * VEC < hi) {
+          const int64_t v0 = tb + (int64_t)(k * NT + tid) * VEC;
+          r[k] = load_stream(reinterpret_cast<const uint4 *>(row + (v0 < hi ? v0 : lo)));
         }
       }
       touch_publish_args<SAMPLE>(a);
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        const bool ok = tb + (int64_t)(k * NT + tid) * VEC < hi;
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) x[k * VEC + e] = ok ? E::at(r[k], e) : -kInf;
+      }
       process(x, tb);
     }
   } else {
@@ -875,10 +885,21 @@ __global__ __launch_bounds__(NT) void token_stats_kernel(StatsArgs a) {
   __shared__ __align__(16) unsigned char slow_scratch[6 * NT * 4];
 
   const int tid = threadIdx.x;
-  const int64_t wg = blockIdx.x;
-  const int64_t row_id = wg / a.slices;
-  const int slice = (int)(wg - row_id * a.slices);
-  const uint32_t b = (uint32_t)(row_id / a.L), l = (uint32_t)(row_id - (int64_t)b * a.L);
+  // The argument fields the prologue needs, in one round of scalar loads (at
+  // the launch's start they all miss the scalar cache, and dependent rounds
+  // add up).
+  asm volatile("" ::"s"(a.logits), "s"(a.row_stride), "s"(a.V), "s"(a.L), "s"(a.slice_len),
+               "s"(a.slices), "s"(a.has_edit), "s"(a.c2));
+  if constexpr (FULL)
+    asm volatile("" ::"s"(a.skip_rows), "s"(a.n_rank_rules), "s"(a.rank_rules[0].mask));
+  // 32-bit index arithmetic: the host limits a launch to fewer than 2^32
+  // workgroups and L to below 2^31.
+  const uint32_t wg = blockIdx.x;
+  const uint32_t ns = (uint32_t)a.slices, nl = (uint32_t)a.L;
+  const uint32_t row32 = ns == 1u ? wg : wg / ns;
+  const int64_t row_id = row32;
+  const int slice = (int)(wg - row32 * ns);
+  const uint32_t b = row32 < nl ? 0u : row32 / nl, l = row32 - b * nl;
   const T *row = reinterpret_cast<const T *>(a.logits) + row_id * a.row_stride;
   const int64_t lo = (int64_t)slice * a.slice_len;
   const int64_t hi = min(lo + a.slice_len, a.V);
