@@ -166,6 +166,7 @@ template <> struct ElemT<uint16_t> {   // bf16 bit patterns
     return (e & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
   }
   __device__ static float load1(const uint16_t *p) { return __uint_as_float((uint32_t)*p << 16); }
+  __device__ static float widen1(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 };
 template <> struct ElemT<float> {
   static constexpr int VEC = 4;
@@ -175,6 +176,7 @@ template <> struct ElemT<float> {
     return __uint_as_float(w);
   }
   __device__ static float load1(const float *p) { return *p; }
+  __device__ static float widen1(float f) { return f; }
 };
 
 // Wave-local running state.  Weights are taken against the reference
@@ -611,13 +613,40 @@ __device__ void stream_slice(const StatsArgs &a, const T *row, int64_t lo, int64
       process(x, tb);
     }
   } else {
-    for (int64_t base = lo; base < hi; base += STEP) {
+    // Rows without 16-byte alignment: one element per load, every load of an
+    // iteration issued before any is used (a lane past the end reads the
+    // slice's first element, its value unused), two register sets in turn.
+    const int64_t n_it = (hi - lo + STEP - 1) / STEP;
+    T ra[U], rb[U];
+    auto ld = [&](T (&r)[U], int64_t it) {
+      const int64_t base = lo + it * STEP;
 #pragma unroll
       for (int k = 0; k < U; ++k) {
         const int64_t v = base + (int64_t)(k * NT + tid);
-        x[k] = (v < hi) ? E::load1(row + v) : -kInf;
+        r[k] = row[v < hi ? v : lo];
       }
+    };
+    auto use = [&](const T (&r)[U], int64_t it) {
+      const int64_t base = lo + it * STEP;
+#pragma unroll
+      for (int k = 0; k < U; ++k)
+        x[k] = base + (int64_t)(k * NT + tid) < hi ? E::widen1(r[k]) : -kInf;
       process(x, base);
+    };
+    ld(ra, 0);
+    int64_t it = 0;
+    for (; it + 2 < n_it; it += 2) {
+      ld(rb, it + 1);
+      use(ra, it);
+      ld(ra, it + 2);
+      use(rb, it + 1);
+    }
+    if (it + 1 < n_it) {
+      ld(rb, it + 1);
+      use(ra, it);
+      use(rb, it + 1);
+    } else {
+      use(ra, it);
     }
   }
 
