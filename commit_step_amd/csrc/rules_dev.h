@@ -345,12 +345,19 @@ __device__ inline RuleCount short_rank_rule(const RuleDev &r, int b, int L, cons
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, nw = sm.nt >> 6;
   const uint8_t *m_row = r.mask + (int64_t)b * L;
   uint8_t *o_row = r.out + (int64_t)b * L;
-  // the score is loaded whatever the mask says, so both loads are in flight
-  // together (one memory round trip, not two)
-  const float cv = t < L ? rule_conf(r, conf + (int64_t)b * L + t) : 0.f;
+  // Score, token and mask are loaded by every thread, whatever the mask
+  // says (threads past the row read its first position, their values
+  // unused), with no branch between the loads: one memory round trip, not
+  // one per load.
+  const bool in_row = t < L;
+  const int tt = in_row ? t : 0;
+  const float cv0 = rule_conf(r, conf + (int64_t)b * L + tt);
+  const int32_t xv = sk.canvas ? load_coherent_i32(sk.x0 + tt) : 0;
+  const uint8_t mv = m_row[tt];
   const int kq = r.kind == DLLM_RULE_TOPK ? r.k[b] : 0;     // in flight with the row's loads
-  if (sk.canvas && t < L) sm.x0s[t] = load_coherent_i32(sk.x0 + t);
-  const bool cand = t < L && m_row[t];
+  const float cv = in_row ? cv0 : 0.f;
+  if (sk.canvas && in_row) sm.x0s[t] = xv;
+  const bool cand = in_row && mv;
   const float c = cand ? conf_sanitized(cv) : 0.f;
   const uint64_t key = cand ? (((uint64_t)conf_key(c) << 32) | (uint32_t)t) : kSentinel;
   int *wcnt = sm.misc, *wfail = sm.misc + 32;
@@ -434,9 +441,15 @@ __device__ inline bool short_entropy_rule(const RuleDev &r, int b, int L, const 
   const int t = threadIdx.x, nt = sm.nt, lane = t & 63, wave = t >> 6, nw = nt >> 6;
   const uint8_t *m_row = r.mask + (int64_t)b * L;
   uint8_t *o_row = r.out + (int64_t)b * L;
-  const float hv = t < L ? load_coherent(ent + (int64_t)b * L + t) : 0.f;   // with the mask
-  if (sk.canvas && t < L) sm.x0s[t] = load_coherent_i32(sk.x0 + t);
-  const bool cand = t < L && m_row[t];
+  // entropy, token and mask in one round trip (as in short_rank_rule)
+  const bool in_row = t < L;
+  const int tt = in_row ? t : 0;
+  const float hv0 = load_coherent(ent + (int64_t)b * L + tt);
+  const int32_t xv = sk.canvas ? load_coherent_i32(sk.x0 + tt) : 0;
+  const uint8_t mv = m_row[tt];
+  const float hv = in_row ? hv0 : 0.f;
+  if (sk.canvas && in_row) sm.x0s[t] = xv;
+  const bool cand = in_row && mv;
   const float h = cand ? hv : 0.f;
   const uint32_t u = __float_as_uint(h);
   const bool bad = cand && u != 0x80000000u && (!bits_finite(u) || (u & 0x80000000u) != 0);
