@@ -143,20 +143,39 @@ __global__ __launch_bounds__(256) void threshold_rows_kernel(RuleDev r, int64_t 
   const double tau = r.taus ? r.taus[b] : r.param;
   int pass = 0;
   uint64_t best = kSentinel;
-#pragma unroll 4
-  for (int l = lane; l < L; l += 64) {
-    const float cv = c_row[l];
-    const uint8_t m = m_row[l];
-    uint8_t v = 0;
-    if (m) {
-      const float c = conf_sanitized(r.negate ? -cv : cv);
-      const double cd = (double)c;
-      v = (r.strict ? (cd > tau) : (cd >= tau)) ? 1 : 0;
-      pass += v;
-      const uint64_t key = ((uint64_t)conf_key(c) << 32) | (uint32_t)l;
-      best = key < best ? key : best;
+  // Eight positions per lane at a time, every load issued before any is used
+  // (a lane past the row reads its first position, the value unused): one
+  // memory round trip per block, not two per position.
+  constexpr int CH = 8;
+  for (int l0 = 0; l0 < L; l0 += 64 * CH) {
+    float cvs[CH];
+    uint32_t ms[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int l = l0 + j * 64 + lane;
+      const int lc = l < L ? l : 0;
+      cvs[j] = c_row[lc];
+      ms[j] = m_row[lc];
     }
-    o_row[l] = v;
+    // every use below depends on this empty asm, so no use (and no wait for
+    // its load) is scheduled between the loads
+#pragma unroll
+    for (int j = 0; j < CH; ++j) asm volatile("" : "+v"(cvs[j]), "+v"(ms[j]));
+    // branch-free use of the loaded values (a branch around a use lets the
+    // compiler sink the load into it, one round trip again)
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int l = l0 + j * 64 + lane;
+      const bool in_row = l < L;
+      const bool cand = in_row && ms[j] != 0;
+      const float c = conf_sanitized(r.negate ? -cvs[j] : cvs[j]);
+      const double cd = (double)c;
+      const bool v = cand && (r.strict ? (cd > tau) : (cd >= tau));
+      pass += v ? 1 : 0;
+      const uint64_t key = cand ? (((uint64_t)conf_key(c) << 32) | (uint32_t)l) : kSentinel;
+      best = key < best ? key : best;
+      if (in_row) o_row[l] = v ? 1 : 0;
+    }
   }
   pass = wave_sum_i(pass);
   best = wave_min_u64(best);
