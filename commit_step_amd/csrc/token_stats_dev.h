@@ -799,9 +799,13 @@ __device__ RowResult slow_row(const StatsArgs &a, const T *row, uint32_t b, uint
 
 // Does any fused rule look at this row?
 __device__ __forceinline__ bool row_needed(const StatsArgs &a, int64_t row_id) {
-  bool need = a.has_edit && a.edit_mask[row_id];
-  for (int r = 0; r < a.n_rank_rules; ++r) need = need || a.rank_rules[r].mask[row_id];
-  return need;
+  // every mask byte is loaded before any is tested (no short-circuit, whose
+  // branch on a loaded byte would cost a round trip per mask)
+  uint32_t need = a.has_edit ? a.edit_mask[row_id] : 0u;
+#pragma unroll
+  for (int r = 0; r < kMaxRules; ++r)
+    need |= r < a.n_rank_rules ? a.rank_rules[r].mask[row_id] : 0u;
+  return need != 0;
 }
 
 // Statistics of a finished row from its merged partial; false when the row is
