@@ -5,7 +5,7 @@ token_stats row of the function table): for every position, the proposed token
 x0, its probability and the entropy of the position's distribution, NaN-safe,
 greedy or Gumbel-max sampling with an explicit key, with ``suppress_ids``.
 
-Readings of the pages taken here (each also listed in the design doc):
+Readings of the pages taken here:
   * suppressed ids are removed before the softmax, so prob and entropy are over
     the remaining vocabulary ("Deviations from the references", suppress_ids item);
   * prob and entropy are those of softmax(logits) as passed; temperature only

@@ -13,8 +13,7 @@ stable and confident.  mlxcel "Block Diffusion", "DiffusionGemma Canvas
 Denoising": stop when the canvas is stable and confident for the configured
 stability window.
 
-Readings taken where the pages give only names and defaults (each also in
-DESIGN.md):
+Readings taken where the pages give only names and defaults:
   * linear_temperature(r, N, t_min, t_max) = t_min + (t_max - t_min) * r / N,
     so the first step (r = N) runs at t_max and the temperature falls
     linearly towards t_min;
