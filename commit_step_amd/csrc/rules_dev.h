@@ -233,70 +233,82 @@ __device__ __forceinline__ void count_below(uint64_t q, const uint64_t *keys, co
 // `extra` for i == n0 < nq.  G = blockDim.x / P threads share a query (P a
 // power of two >= max(nq, 64), so each wave works on one part of the list);
 // the owner, thread i < P, returns the count, the value sum and its query.
-template <bool VALS>
+// Transposed ranks of up to 64 QPL queries: each wave scans a 1/nw share of
+// the list for QPL queries per lane (query lane + 64 u), so every key read
+// serves QPL comparisons.  The per-wave counts and sums meet in LDS atomics on
+// part_cnt / part_sum, which the caller zeroed before its compaction barrier
+// (both hold at least 64 QPL entries: one per thread of the workgroup).
+// Counts are exact; the float64 sums then add in any order, which the
+// callers' error bound already allows for.
+template <bool VALS, int QPL>
+__device__ inline int transposed_rank(int nq, int n0, uint64_t extra, const uint64_t *list, int n,
+                                      const double *vals, const RuleSmem &sm, double &sum,
+                                      uint64_t &query) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6, nw = sm.nt >> 6;
+  const int per = (n + nw - 1) / nw;
+  const int j0 = min(wave * per, n), j1 = min(j0 + per, n);
+  uint64_t qk[QPL];
+  int c[QPL];
+  double sq[QPL];
+#pragma unroll
+  for (int u = 0; u < QPL; ++u) {
+    const int i = lane + 64 * u;
+    qk[u] = i < n0 ? list[i] : (i < nq ? extra : 0ull);   // 0: no key lies below
+    c[u] = 0;
+    sq[u] = 0.0;
+  }
+  int j = j0;
+  for (; j + 4 <= j1; j += 4) {
+    uint64_t k[4];
+    double v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      k[e] = list[j + e];
+      if constexpr (VALS) v[e] = vals[j + e];
+    }
+#pragma unroll
+    for (int u = 0; u < QPL; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool lt = k[e] < qk[u];
+        c[u] += (int)lt;
+        if constexpr (VALS) sq[u] += lt ? v[e] : 0.0;
+      }
+  }
+  for (; j < j1; ++j) {
+    const uint64_t k = list[j];
+#pragma unroll
+    for (int u = 0; u < QPL; ++u) {
+      const bool lt = k < qk[u];
+      c[u] += (int)lt;
+      if constexpr (VALS) sq[u] += lt ? vals[j] : 0.0;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < QPL; ++u) {
+    const int i = lane + 64 * u;
+    if (i < nq) {
+      if (c[u]) atomicAdd(&sm.part_cnt[i], c[u]);
+      if (VALS && sq[u] != 0.0) atomicAdd(&sm.part_sum[i], sq[u]);
+    }
+  }
+  __syncthreads();
+  query = t < n0 ? list[t] : (t < nq ? extra : kSentinel);
+  sum = (VALS && t < nq) ? sm.part_sum[t] : 0.0;
+  return t < nq ? sm.part_cnt[t] : 0;
+}
+
+// WIDE: also the transposed form for up to 512 queries (eight per lane); only
+// the standalone rule kernels take it, since a second inlined copy of the
+// transposed loop makes the fused kernels copy their argument block to scratch.
+template <bool VALS, bool WIDE = false>
 __device__ inline int block_rank(int nq, int n0, uint64_t extra, const uint64_t *list, int n,
                                  const double *vals, const RuleSmem &sm, int P, double &sum,
                                  uint64_t &query) {
-  if (nq <= 256) {
-    // Transposed: each wave scans a 1/nw share of the list for up to four
-    // queries per lane (query lane + 64 q), so every key read serves four
-    // comparisons.  The per-wave counts and sums meet in LDS atomics on
-    // part_cnt / part_sum, which the caller zeroed before its compaction
-    // barrier.  Counts are exact; the float64 sums then add in any order,
-    // which the callers' error bound already allows for.
-    const int t = threadIdx.x, lane = t & 63, wave = t >> 6, nw = sm.nt >> 6;
-    const int per = (n + nw - 1) / nw;
-    const int j0 = min(wave * per, n), j1 = min(j0 + per, n);
-    uint64_t qk[4];
-    int c[4];
-    double sq[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = lane + 64 * u;
-      qk[u] = i < n0 ? list[i] : (i < nq ? extra : 0ull);   // 0: no key lies below
-      c[u] = 0;
-      sq[u] = 0.0;
-    }
-    int j = j0;
-    for (; j + 4 <= j1; j += 4) {
-      uint64_t k[4];
-      double v[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        k[e] = list[j + e];
-        if constexpr (VALS) v[e] = vals[j + e];
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool lt = k[e] < qk[u];
-          c[u] += (int)lt;
-          if constexpr (VALS) sq[u] += lt ? v[e] : 0.0;
-        }
-    }
-    for (; j < j1; ++j) {
-      const uint64_t k = list[j];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const bool lt = k < qk[u];
-        c[u] += (int)lt;
-        if constexpr (VALS) sq[u] += lt ? vals[j] : 0.0;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int i = lane + 64 * u;
-      if (i < nq) {
-        if (c[u]) atomicAdd(&sm.part_cnt[i], c[u]);
-        if (VALS && sq[u] != 0.0) atomicAdd(&sm.part_sum[i], sq[u]);
-      }
-    }
-    __syncthreads();
-    query = t < n0 ? list[t] : (t < nq ? extra : kSentinel);
-    sum = (VALS && t < nq) ? sm.part_sum[t] : 0.0;
-    return t < nq ? sm.part_cnt[t] : 0;
-  }
+  if (nq <= 256) return transposed_rank<VALS, 4>(nq, n0, extra, list, n, vals, sm, sum, query);
+  if constexpr (WIDE)
+    if (nq <= 512 && sm.nt >= 512)
+      return transposed_rank<VALS, 8>(nq, n0, extra, list, n, vals, sm, sum, query);
   const int t = threadIdx.x, G = sm.nt / P, part = t / P, i = t - part * P;
   const int per = (n + G - 1) / G;
   const int j0 = min(part * per, n), j1 = min(j0 + per, n);
@@ -340,6 +352,7 @@ __device__ __forceinline__ int slots_sum(const int *slots, int nw, int wave, int
 }
 
 // topk / factor on a short row.
+template <bool WIDE = false>
 __device__ inline RuleCount short_rank_rule(const RuleDev &r, int b, int L, const float *conf,
                                             const RuleSmem &sm, const CommitSink &sk) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, nw = sm.nt >> 6;
@@ -406,7 +419,7 @@ __device__ inline RuleCount short_rank_rule(const RuleDev &r, int b, int L, cons
   const int P = owners_for(n, sm.nt);
   double unused;
   uint64_t q;
-  const int rank = block_rank<false>(n, n, kSentinel, sm.keys, n, nullptr, sm, P, unused, q);
+  const int rank = block_rank<false, WIDE>(n, n, kSentinel, sm.keys, n, nullptr, sm, P, unused, q);
   const bool owner = t < n;     // thread t < n owns query t
   int n_commit;
   if (r.kind == DLLM_RULE_TOPK) {
@@ -435,6 +448,7 @@ __device__ inline RuleCount short_rank_rule(const RuleDev &r, int b, int L, cons
 // sorted path.  Entropies being >= 0, only candidates with H <= gamma can be
 // followed by another committed one, so ranks and prefix sums run over that
 // subset F plus the smallest key above gamma.
+template <bool WIDE = false>
 __device__ inline bool short_entropy_rule(const RuleDev &r, int b, int L, const float *ent,
                                           const RuleSmem &sm, const CommitSink &sk,
                                           RuleCount &rc) {
@@ -535,7 +549,7 @@ __device__ inline bool short_entropy_rule(const RuleDev &r, int b, int L, const 
   const int P = owners_for(nq, nt);
   double S;
   uint64_t q;
-  const int rank = block_rank<true>(nq, nF, nxt, sm.keys, nF, sm.hs, sm, P, S, q);
+  const int rank = block_rank<true, WIDE>(nq, nF, nxt, sm.keys, nF, sm.hs, sm, P, S, q);
   const bool live = t < nq;     // thread t < nq owns query t
   // Entropies are >= 0, so sum |h| = S: |S - exact| <= (terms + 64) 2^-53 S
   // whatever the summation order.
@@ -740,6 +754,7 @@ __device__ inline RuleCount rule_threshold(const RuleDev &r, int b, int L, const
 // Runs a ranking rule on batch row b.  Every thread of the workgroup must call
 // it.  `conf` is the confidence (prob) array and `ent` the entropy array.
 // Returns the candidate and commit counts (valid in thread 0).
+template <bool WIDE = false>
 __device__ inline RuleCount run_batch_rule(const RuleDev &r, int b, int L, const float *conf,
                                            const float *ent, unsigned char *smem,
                                            const CommitSink &sk, int nt) {
@@ -752,11 +767,11 @@ __device__ inline RuleCount run_batch_rule(const RuleDev &r, int b, int L, const
       break;
     case DLLM_RULE_TOPK:
     case DLLM_RULE_FACTOR:
-      if (short_row) rc = short_rank_rule(r, b, L, conf, sm, sk);
+      if (short_row) rc = short_rank_rule<WIDE>(r, b, L, conf, sm, sk);
       else rc = long_rank_rule(r, b, L, conf, sm, sk);
       break;
     case DLLM_RULE_ENTROPY_BOUND: {
-      const bool done = short_row && short_entropy_rule(r, b, L, ent, sm, sk, rc);
+      const bool done = short_row && short_entropy_rule<WIDE>(r, b, L, ent, sm, sk, rc);
       if (!done) {
         __syncthreads();
         rc = long_entropy_rule(r, b, L, ent, sm, sk);

@@ -125,7 +125,7 @@ template <int NT>
 __global__ __launch_bounds__(NT) void batch_rule_kernel(RuleDev r, int L, const float *conf,
                                                         const float *ent) {
   extern __shared__ __align__(16) unsigned char smem[];
-  run_batch_rule(r, (int)blockIdx.x, L, conf, ent, smem, CommitSink{nullptr, nullptr}, NT);
+  run_batch_rule<true>(r, (int)blockIdx.x, L, conf, ent, smem, CommitSink{nullptr, nullptr}, NT);
 }
 
 // The standalone threshold rule: one wave per batch row, four rows per
