@@ -192,3 +192,38 @@ def test_llada_block_loop_runs_on_the_device():
             assert_stats((gx, gp, ge), ref, "bf16", f"llada step {s}", mask=cand)
     assert not (tokens == mask_id).any()
     log("llada block loop: 32 steps, all committed")
+
+
+@pytest.mark.parametrize("i", range(48))
+def test_random_commit_steps(i):
+    """Seeded random commit steps: dtype, shape (odd and split vocabularies,
+    short and long batch rows), rank rule and its parameter, edit rule or none,
+    row skipping or not, greedy or sampled; rows no rule looks at hold NaN when
+    they are skipped."""
+    rng = np.random.default_rng(7000 + i)
+    dtype = "bf16" if rng.random() < 0.6 else "f32"
+    V = int(rng.choice([64, 1001, 4096, 5003, 9000, 20000, 40000]))
+    B = int(rng.integers(1, 4))
+    L = int(rng.choice([8, 32, 64, 100, 256, 300]))
+    kind = str(rng.choice(["threshold", "topk", "factor", "entropy_bound", "none"]))
+    with_edit = bool(rng.random() < 0.5) or kind == "none"
+    skip_rows = bool(rng.random() < 0.6)
+    T = 0.0 if rng.random() < 0.6 else float(np.float32(rng.uniform(0.5, 1.2)))
+    mask_id = V - 1
+    tokens, masked, editable = _canvas(rng, B, L, V, mask_id, P=L // 8,
+                                       frac_masked=float(rng.uniform(0.2, 0.9)))
+    bits, _ = random_logits(8000 + i, B, L, V, dtype, float(rng.uniform(1.0, 3.5)), 0.5, 4.0,
+                            14.0, (mask_id,))
+    arr = bits.copy()
+    if skip_rows:
+        nan = np.uint16(0x7FC0) if dtype == "bf16" else np.float32(np.nan)
+        arr[~(masked | (editable if with_edit else False))] = nan
+    param = {"threshold": float(rng.choice([0.5, 0.9])), "topk": int(rng.integers(0, 9)),
+             "factor": float(rng.choice([0.5, 1.0, 2.0])),
+             "entropy_bound": float(rng.choice([0.2, 0.5, 1.5])), "none": None}[kind]
+    strict = bool(rng.integers(2))
+    _run_and_check(arr, dtype, tokens, masked, editable if with_edit else None,
+                   None if kind == "none" else kind, param, strict if kind == "threshold" else False,
+                   T=T, seed=int(rng.integers(0, 2 ** 40)) if T > 0 else None,
+                   step=int(rng.integers(0, 50)), sup=(mask_id,), skip_rows=skip_rows,
+                   label=f"random {i}")
