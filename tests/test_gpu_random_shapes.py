@@ -84,3 +84,39 @@ def test_random_fused_launch(i):
     else:
         want = oracle.entropy_bound_transfer(gpu[2], c["cand"], gamma)
     assert np.array_equal(mask, want), f"case {i}: fused {kind} mask differs from the oracle's"
+
+
+@pytest.mark.parametrize("i", range(40))
+def test_random_margin_argmax_and_statistics_temperature(i):
+    """Seeded random launches with the margin, the greedy argmax beside a
+    sampled x0, and a statistics temperature: margin with prob and entropy
+    within the dtype tolerance, argmax bit-exact."""
+    rng = np.random.default_rng(50000 + i)
+    dtype = "bf16" if rng.random() < 0.6 else "f32"
+    V = int(rng.choice([2, 7, 1000, 4096, 5003, 9000, 33000]))
+    B, L = int(rng.integers(1, 4)), int(rng.choice([1, 5, 40, 100]))
+    n_sup = int(rng.integers(0, min(4, V - 1) + 1))
+    sup = tuple(sorted(set(int(v) for v in rng.choice(V, size=n_sup, replace=False)))) \
+        if n_sup else ()
+    T = 0.0 if rng.random() < 0.5 else float(np.float32(rng.uniform(0.5, 1.5)))
+    Ts = float(np.float32(rng.choice([1.0, 0.5, 0.8, 1.7])))
+    seed = int(rng.integers(0, 2 ** 40)) if T > 0 else None
+    bits, _ = random_logits(60000 + i, B, L, V, dtype, float(rng.uniform(0.5, 4.0)), 0.4, 2.0,
+                            12.0, sup)
+    log(f"case {i}: {dtype} B={B} L={L} V={V} T={T} Ts={Ts} suppress={len(sup)}")
+    st = dc.token_stats(to_dev(bits, dtype), temperature=T, seed=seed, step=3, suppress_ids=sup,
+                        margin=True, argmax=True, stats_temperature=Ts)
+    g = stats_np(st)
+    am = st.argmax.cpu().numpy()
+    ref = oracle.token_stats(bits, dtype, temperature=T, seed=seed, step=3, suppress_ids=sup,
+                             stats_temperature=Ts)
+    greedy = oracle.token_stats(bits, dtype, suppress_ids=sup, stats_temperature=Ts)
+    assert np.array_equal(am, greedy.x0), f"case {i}: argmax"
+    fields = ("prob", "entropy", "margin")
+    if T > 0:
+        pos = [(b, l) for b in range(B) for l in range(L)]
+        assert_sampled_x0(g[0], ref.x0, bits, dtype, T, seed, 3, sup, pos, f"case {i}")
+        assert_stats(g, ref, dtype, f"case {i}", mask=(g[0] == ref.x0), x0_exact=False,
+                     fields=fields)
+    else:
+        assert_stats(g, ref, dtype, f"case {i}", fields=fields)
