@@ -167,12 +167,27 @@ def workspace_size(logits):
         return int(load_library().dllm_token_stats_workspace_size(dt, B, L, V))
 
 
-def _workspace(device, nbytes):
-    """A zero-filled byte buffer per device, grown on demand.  The library
-    leaves it zero-filled after every successful call."""
-    key = (device.type, device.index)
+def _capturing(device):
+    return device.type == "cuda" and torch.cuda.is_current_stream_capturing()
+
+
+def _workspace(device, stream, nbytes):
+    """The default workspace: a zero-filled byte buffer per (device, stream),
+    grown on demand.  The library leaves it zero-filled after every
+    successful call.  Calls in flight at the same time must not share a
+    workspace (their row and batch-row counters would mix), and calls on one
+    stream never overlap, so one buffer per stream is safe.  A buffer cannot
+    be created or grown while the stream is being captured into a graph (the
+    zero fill would become a node of the graph): make one eager call of the
+    same or a larger shape first, or pass ``workspace=``."""
+    key = (device.type, device.index, stream)
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
+        if _capturing(device):
+            raise RuntimeError(
+                "the default workspace of this stream has to be created or grown during graph "
+                "capture; make one eager call of this shape on the stream first, or pass "
+                "workspace= (zero-filled, workspace_size() bytes)")
         ws = torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
         _workspaces[key] = ws
     return ws
@@ -361,17 +376,18 @@ def _stats_call(logits, temperature, seed, step, suppress_ids, rules, out, works
     lib = load_library()
     with _on(dev):
         need = _ws_size(dt, B, L, V, dev)
-        ws = workspace if workspace is not None else _workspace(dev, need)
+        stream = _stream(logits)
+        ws = workspace if workspace is not None else _workspace(dev, stream, need)
         args = [logits.data_ptr(), dt, B, L, V, row_stride, float(temperature),
                 int(seed or 0) & 0xFFFFFFFFFFFFFFFF, int(step), sup, len(suppress_ids),
                 x0.data_ptr(), prob.data_ptr(), ent.data_ptr(), ctypes.byref(extra),
                 crules if len(rules) else None, len(rules)]
         if canvas is None:
-            _check(lib.dllm_token_stats(*args, ws.data_ptr(), ws.numel(), _stream(logits)),
+            _check(lib.dllm_token_stats(*args, ws.data_ptr(), ws.numel(), stream),
                    "dllm_token_stats")
         else:
             _check(lib.dllm_commit_step(*args, ctypes.byref(canvas[0]), ws.data_ptr(),
-                                        ws.numel(), _stream(logits)), "dllm_commit_step")
+                                        ws.numel(), stream), "dllm_commit_step")
     return Stats(x0, prob, ent, mar, am)
 
 

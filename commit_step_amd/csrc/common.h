@@ -18,6 +18,12 @@ int ok();
 int check_launch(const char *what);
 // Compute units of the current device (cached per device).
 int device_cu_count();
+// DLLM_ERR_UNSUPPORTED, with a message naming `who`, if a launch of `kernel`
+// with `dynamic_lds` bytes of dynamic LDS would exceed the current device's
+// LDS per workgroup (static size cached per kernel); a launch that asks for
+// more makes the runtime abort the queue.  DLLM_ERR_HIP if the sizes cannot be
+// queried; else DLLM_OK.
+int check_lds(const void *kernel, size_t dynamic_lds, const char *who);
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;

@@ -53,19 +53,13 @@ size_t workspace_bytes_for(int64_t B, int64_t L, int slices) {
   return bytes;
 }
 
-template <typename T, int NT, int UV>
-hipError_t launch_t(const Plan &p, const StatsArgs &a, int64_t rows, bool sample, size_t smem,
-                    hipStream_t s) {
-  return launch_f<T, NT, UV, false>(p, a, rows, sample, smem, s);
-}
-
 // Dispatch on the plan's (threads, loads per chunk).
 template <typename T>
-hipError_t launch_plan(const Plan &p, const StatsArgs &a, int64_t rows, bool sample, size_t smem,
-                       hipStream_t s) {
+int launch_plan(const Plan &p, const StatsArgs &a, int64_t rows, bool sample, size_t smem,
+                hipStream_t s, const char *who) {
   constexpr int U0 = ElemT<T>::U;
-  if (p.nt == 512) return launch_t<T, 512, U0>(p, a, rows, sample, smem, s);
-  return launch_t<T, 256, U0>(p, a, rows, sample, smem, s);
+  if (p.nt == 512) return launch_f<T, 512, U0, false>(p, a, rows, sample, smem, s, who);
+  return launch_f<T, 256, U0, false>(p, a, rows, sample, smem, s, who);
 }
 
 }  // namespace
@@ -238,13 +232,9 @@ int stats_step(const char *who, const void *logits, int dtype, int64_t B, int64_
   const bool sample = temperature > 0.0f;
   size_t smem = a.n_rank_rules ? rule_smem_bytes((int)L, p.nt) : 0;
   if (p.slices > 1) smem = std::max(smem, (size_t)p.slices * sizeof(Partial));
-  hipError_t e;
-  if (a.skip_rows || a.margin) e = launch_full(dtype, p, a, rows, sample, smem, stream);
-  else if (dtype == DLLM_BF16) e = launch_plan<uint16_t>(p, a, rows, sample, smem, stream);
-  else e = launch_plan<float>(p, a, rows, sample, smem, stream);
-  if (e != hipSuccess)
-    return fail(DLLM_ERR_HIP, "%s: launch failed: %s", who, hipGetErrorString(e));
-  return ok();
+  if (a.skip_rows || a.margin) return launch_full(dtype, p, a, rows, sample, smem, stream, who);
+  if (dtype == DLLM_BF16) return launch_plan<uint16_t>(p, a, rows, sample, smem, stream, who);
+  return launch_plan<float>(p, a, rows, sample, smem, stream, who);
 }
 
 }  // namespace

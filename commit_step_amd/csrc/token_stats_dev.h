@@ -1032,22 +1032,25 @@ struct Plan {
   bool vec;
 };
 
+// Launch of the plan's kernel, after checking that its LDS (static + smem
+// dynamic bytes) fits the device; returns a DLLM status.
 template <typename T, int NT, int UV, bool FULL>
-hipError_t launch_f(const Plan &p, const StatsArgs &a, int64_t rows, bool sample, size_t smem,
-                    hipStream_t s) {
+int launch_f(const Plan &p, const StatsArgs &a, int64_t rows, bool sample, size_t smem,
+             hipStream_t s, const char *who) {
   dim3 grid((unsigned)(rows * p.slices)), block(NT);
-  if (sample) {
-    if (p.vec) token_stats_kernel<T, NT, UV, true, true, FULL><<<grid, block, smem, s>>>(a);
-    else token_stats_kernel<T, NT, UV, true, false, FULL><<<grid, block, smem, s>>>(a);
-  } else {
-    if (p.vec) token_stats_kernel<T, NT, UV, false, true, FULL><<<grid, block, smem, s>>>(a);
-    else token_stats_kernel<T, NT, UV, false, false, FULL><<<grid, block, smem, s>>>(a);
-  }
-  return hipGetLastError();
+  void (*kern)(StatsArgs) =
+      sample ? (p.vec ? token_stats_kernel<T, NT, UV, true, true, FULL>
+                      : token_stats_kernel<T, NT, UV, true, false, FULL>)
+             : (p.vec ? token_stats_kernel<T, NT, UV, false, true, FULL>
+                      : token_stats_kernel<T, NT, UV, false, false, FULL>);
+  const int lds = check_lds((const void *)kern, smem, who);
+  if (lds != DLLM_OK) return lds;
+  kern<<<grid, block, smem, s>>>(a);
+  return check_launch(who);
 }
 
 // The FULL = true kernels, instantiated in token_stats_full.hip.
-hipError_t launch_full(int dtype, const Plan &p, const StatsArgs &a, int64_t rows, bool sample,
-                       size_t smem, hipStream_t s);
+int launch_full(int dtype, const Plan &p, const StatsArgs &a, int64_t rows, bool sample,
+                size_t smem, hipStream_t s, const char *who);
 
 }  // namespace dllm

@@ -8,19 +8,19 @@ namespace dllm {
 namespace {
 
 template <typename T>
-hipError_t launch_full_t(const Plan &p, const StatsArgs &a, int64_t rows, bool sample,
-                         size_t smem, hipStream_t s) {
+int launch_full_t(const Plan &p, const StatsArgs &a, int64_t rows, bool sample, size_t smem,
+                  hipStream_t s, const char *who) {
   constexpr int U0 = ElemT<T>::U;
-  if (p.nt == 512) return launch_f<T, 512, U0, true>(p, a, rows, sample, smem, s);
-  return launch_f<T, 256, U0, true>(p, a, rows, sample, smem, s);
+  if (p.nt == 512) return launch_f<T, 512, U0, true>(p, a, rows, sample, smem, s, who);
+  return launch_f<T, 256, U0, true>(p, a, rows, sample, smem, s, who);
 }
 
 }  // namespace
 
-hipError_t launch_full(int dtype, const Plan &p, const StatsArgs &a, int64_t rows, bool sample,
-                       size_t smem, hipStream_t s) {
-  if (dtype == DLLM_BF16) return launch_full_t<uint16_t>(p, a, rows, sample, smem, s);
-  return launch_full_t<float>(p, a, rows, sample, smem, s);
+int launch_full(int dtype, const Plan &p, const StatsArgs &a, int64_t rows, bool sample,
+                size_t smem, hipStream_t s, const char *who) {
+  if (dtype == DLLM_BF16) return launch_full_t<uint16_t>(p, a, rows, sample, smem, s, who);
+  return launch_full_t<float>(p, a, rows, sample, smem, s, who);
 }
 
 }  // namespace dllm

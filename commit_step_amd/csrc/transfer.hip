@@ -12,6 +12,9 @@
 #include <string.h>
 
 #include "common.h"
+#include <mutex>
+#include <unordered_map>
+
 #include "rules_dev.h"
 
 namespace dllm {
@@ -37,6 +40,39 @@ int check_launch(const char *what) {
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(DLLM_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
   return ok();
+}
+
+int check_lds(const void *kernel, size_t dynamic_lds, const char *who) {
+  static std::mutex mu;
+  static std::unordered_map<const void *, size_t> static_lds;
+  static int limit[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+    return fail(DLLM_ERR_HIP, "%s: no current device", who);
+  size_t fixed = 0;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = static_lds.find(kernel);
+    if (it == static_lds.end()) {
+      hipFuncAttributes attr;
+      if (hipFuncGetAttributes(&attr, kernel) != hipSuccess)
+        return fail(DLLM_ERR_HIP, "%s: cannot query the kernel's LDS size", who);
+      it = static_lds.emplace(kernel, attr.sharedSizeBytes).first;
+    }
+    fixed = it->second;
+    if (limit[dev] == 0) {
+      int n = 0;
+      if (hipDeviceGetAttribute(&n, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+          n <= 0)
+        return fail(DLLM_ERR_HIP, "%s: cannot query the device's LDS size", who);
+      limit[dev] = n;
+    }
+  }
+  if (fixed + dynamic_lds > (size_t)limit[dev])
+    return fail(DLLM_ERR_UNSUPPORTED,
+                "%s: the launch needs %zu bytes of LDS (%zu static + %zu dynamic), more than the "
+                "device's %d per workgroup", who, fixed + dynamic_lds, fixed, dynamic_lds, limit[dev]);
+  return DLLM_OK;
 }
 
 int device_cu_count() {
@@ -256,6 +292,11 @@ static int launch_batch_rule(const dllm_rule &rule, int64_t B, int64_t L, const 
   if (B > (int64_t)(0xffffffffu / (unsigned)nt))
     return fail(DLLM_ERR_UNSUPPORTED, "%s: B = %lld batch rows exceeds the launch limit", who, (long long)B);
   const size_t smem = rule_smem_bytes((int)L, nt);
+  const void *kern = nt == 1024 ? (const void *)&batch_rule_kernel<1024>
+                     : nt == 512 ? (const void *)&batch_rule_kernel<512>
+                                 : (const void *)&batch_rule_kernel<256>;
+  const int lds = check_lds(kern, smem, who);
+  if (lds != DLLM_OK) return lds;
   if (nt == 1024)
     batch_rule_kernel<1024><<<dim3((unsigned)B), dim3(1024), smem, s>>>(d, (int)L, scores, scores);
   else if (nt == 512)

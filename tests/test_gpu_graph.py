@@ -99,3 +99,45 @@ def test_graph_replays_match_eager_results():
             assert torch.equal(got[name], t), f"replay {rep}: {name} differs from the eager run"
         assert int(torch.count_nonzero(ws)) == 0, f"replay {rep}: workspace left dirty"
     log("graph replays match the eager run")
+
+
+def test_graph_with_the_default_workspace_of_the_capture_stream():
+    """No workspace= argument: the call takes its stream's default workspace,
+    created by an eager call on the capture stream before the capture."""
+    dev = torch.device("cuda:0")
+    B, L, V = 2, 48, 30000                                       # split rows
+    lg = to_dev(random_logits(95, B, L, V, "bf16", 2.0, 0.5, 6.0, 14.0)[0], "bf16")
+    cand = torch.ones((B, L), dtype=torch.bool, device=dev)
+    out = (torch.empty((B, L), dtype=torch.int32, device=dev),
+           torch.empty((B, L), dtype=torch.float32, device=dev),
+           torch.empty((B, L), dtype=torch.float32, device=dev))
+    masks = {}
+
+    def call():
+        r = dc.Rule.entropy_bound(cand, 0.5)
+        dc.token_stats(lg, rules=[r], out=out)
+        masks["eb"] = r.out
+
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(cap):
+        call()                                       # creates the capture stream's workspace
+    torch.cuda.current_stream().wait_stream(cap)
+    torch.cuda.synchronize()
+    want = [t.clone() for t in out] + [masks["eb"].clone()]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        call()
+    graph_mask = masks["eb"]                         # the captured call's output
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in out:
+            t.fill_(7)
+        call()                                       # eager call on the default stream
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = list(out) + [graph_mask]
+        for i, (a, b) in enumerate(zip(got, want)):
+            assert torch.equal(a, b), f"replay {rep}: output {i} differs from the eager run"
+    log("default-workspace graph replays match the eager run")

@@ -4,7 +4,10 @@ Every kernel must run without scratch memory: a private segment makes each
 launch set up scratch, and in this code it has meant the whole argument block
 copied to scratch (the optimizer gives up proving it read-only once the
 kernel grows).  The greedy streaming kernels must keep two waves per SIMD at
-512 threads (at most 256 VGPRs) and four at 256 (at most 128)."""
+512 threads (at most 256 VGPRs) and four at 256 (at most 128).  Every
+kernel's static LDS plus the most dynamic LDS its launcher can ask for must
+fit the 160 KiB a gfx950 workgroup may hold: a launch beyond it is not an
+error the runtime returns but an aborted queue."""
 import os
 import re
 import subprocess
@@ -23,16 +26,57 @@ SOURCES = ["token_stats.hip", "token_stats_full.hip", "transfer.hip", "uniform.h
 
 
 def _parse(path):
-    found, cur = {}, None
-    for line in open(path).read().splitlines():     # the amdhsa metadata, one kernel at a time
-        m = re.match(r"\s+\.name:\s+(_Z\S+)$", line)
-        if m:
-            cur = found.setdefault(m.group(1), {})
+    """Per-kernel fields of the amdhsa metadata: the kernels are a YAML list
+    whose items open with '  - ' at two spaces, each item's keys in
+    alphabetical order (so fields before `.name` belong to the same item)."""
+    text = open(path).read()
+    meta = text[text.index("amdhsa.kernels:"):text.index("amdhsa.target")]
+    found = {}
+    for block in re.split(r"\n  - ", meta)[1:]:
+        m = re.search(r"^\s+\.name:\s+(_Z\S+)$", block, re.M)
+        if not m:
             continue
-        m = re.match(r"\s+\.(private_segment_fixed_size|vgpr_count|sgpr_count):\s+(\d+)$", line)
-        if m and cur is not None:
-            cur[m.group(1)] = int(m.group(2))
+        fields = {}
+        for key in ("private_segment_fixed_size", "group_segment_fixed_size", "vgpr_count",
+                    "sgpr_count"):
+            f = re.search(r"^\s+\." + key + r":\s+(\d+)$", block, re.M)
+            fields[key] = int(f.group(1)) if f else None
+        found[m.group(1)] = fields
     return found
+
+
+def _const(path, pattern):
+    m = re.search(pattern, open(path).read(), re.M)
+    assert m, f"{pattern} not found in {path}"
+    return int(m.group(1))
+
+
+MAX_L = _const(os.path.join(ROOT, "include", "dllm_commit.h"), r"^#define DLLM_MAX_L (\d+)")
+MAX_SLICES = _const(os.path.join(CSRC, "token_stats_dev.h"), r"kMaxSlices = (\d+);")
+PARTIAL_BYTES = 32      # sizeof(Partial), asserted in token_stats_dev.h
+LDS_LIMIT = 160 * 1024  # LDS per workgroup on gfx950
+
+
+def _rule_lds(L, nt):
+    """Dynamic LDS of the ranking rules for a batch row of L positions run by
+    nt threads (rule_smem_bytes in rules_dev.h: position lists of 20 bytes
+    per slot of the power-of-two padded row plus 12 bytes per thread, or the
+    8-byte sort keys, whichever is larger, plus 512 bytes of flags)."""
+    npow = 64
+    while npow < L:
+        npow *= 2
+    return ((max(npow * 20 + nt * 12, npow * 8) + 7) & ~7) + 512
+
+
+def _max_dynamic_lds(name):
+    """The largest dynamic LDS request the library makes for this kernel."""
+    m = re.search(r"token_stats_kernelI[tf]Li(\d+)E", name)
+    if m:   # ranking rules fused into the last group of a batch row, or slice partials
+        return max(_rule_lds(MAX_L, int(m.group(1))), MAX_SLICES * PARTIAL_BYTES)
+    m = re.search(r"batch_rule_kernelILi(\d+)E", name)
+    if m:
+        return _rule_lds(MAX_L, int(m.group(1)))
+    return 0
 
 
 @pytest.fixture(scope="module")
@@ -69,3 +113,41 @@ def test_no_scratch_and_vgpr_budget(src, kernels):
         if m:
             budget = 256 if m.group(1) == "512" else 128
             assert r["vgpr_count"] <= budget, f"{name}: {r}"
+
+
+@pytest.mark.parametrize("src", SOURCES)
+def test_lds_fits_workgroup(src, kernels):
+    ks = kernels[src]
+    assert ks, f"no kernels found in {src}"
+    for name, r in ks.items():
+        assert r["group_segment_fixed_size"] is not None, f"{name}: no LDS size in metadata"
+        need = r["group_segment_fixed_size"] + _max_dynamic_lds(name)
+        assert need <= LDS_LIMIT, f"{name}: {need} bytes of LDS ({r})"
+
+
+def test_parse_attributes_fields_to_their_own_kernel(tmp_path):
+    """Keys sorted before `.name` in a metadata item belong to that item."""
+    meta = """\t.amdgpu_metadata
+---
+amdhsa.kernels:
+  - .args: []
+    .group_segment_fixed_size: 100
+    .name:           _Z1av
+    .private_segment_fixed_size: 0
+    .sgpr_count:     10
+    .vgpr_count:     20
+  - .args: []
+    .group_segment_fixed_size: 200
+    .name:           _Z1bv
+    .private_segment_fixed_size: 16
+    .sgpr_count:     30
+    .vgpr_count:     40
+amdhsa.target:   amdgcn-amd-amdhsa--gfx950
+"""
+    p = tmp_path / "k.s"
+    p.write_text(meta)
+    got = _parse(str(p))
+    assert got["_Z1av"] == {"private_segment_fixed_size": 0, "group_segment_fixed_size": 100,
+                            "vgpr_count": 20, "sgpr_count": 10}
+    assert got["_Z1bv"] == {"private_segment_fixed_size": 16, "group_segment_fixed_size": 200,
+                            "vgpr_count": 40, "sgpr_count": 30}
