@@ -8,12 +8,18 @@ edit (tau 0.9, 102 committed positions).  A step is that launch.
 
 Inputs are resident in HBM before the timed region; the launch rotates over
 --rotate copies of the logits (default 8 x 128 MiB = 1 GiB) so the 256 MB
-Infinity Cache cannot serve repeated reads.  Exactly --steps launches are
-timed with HIP events on the stream they are enqueued on.
+Infinity Cache cannot serve repeated reads.  Before the step, a plain read of
+the same copies (the read ceiling, 2 x 2000 launches) is timed; then --warmup
+untimed launches, then exactly --steps launches timed with one pair of HIP
+events on the stream they are enqueued on (value, ms_per_step), then the same
+number of launches again (at least 20 groups of 25) in groups of 25
+back-to-back launches, each group between its own pair of events
+(per_launch: the median of the group means, the roofline's time per launch).
 
 Prints one JSON line: logit GB/s (value), positions/s, steps/s, the roofline
 of the kernel against the 8 TB/s HBM peak, and the oracle's throughput on
-the host cores (cpu_baseline).
+the host cores (cpu_baseline: a fork pool over this process's cores, taken
+before the GPU is touched, with the one-worker figure beside it).
 """
 import argparse
 import ctypes
@@ -42,10 +48,13 @@ def parse_args():
                    help="minimum host time spent timing the oracle")
     p.add_argument("--copy-probe", action="store_true",
                    help="only run a plain 1 GiB device copy (counter calibration)")
+    p.add_argument("--ceiling-launches", type=int, default=2000,
+                   help="launches of each plain-read ceiling measurement")
     p.add_argument("--workload", default="diffusiongemma_canvas",
-                   choices=["diffusiongemma_canvas", "llada_block_loop", "tiny", "dream_canvas",
-                            "batched"],
-                   help="diffusiongemma_canvas (default, the headline step); llada_block_loop "
+                   choices=["diffusiongemma_canvas", "diffusiongemma_stats", "llada_block_loop",
+                            "tiny", "dream_canvas", "batched"],
+                   help="diffusiongemma_canvas (default, the headline step); diffusiongemma_stats "
+                        "(the same canvas, dllm_token_stats with no rule fused); llada_block_loop "
                         "(the 32-step LLaDA block with dllm_commit_step); tiny (1 x 64 x 4096 "
                         "fp32, threshold); dream_canvas (4 x 256 x 151936 bf16, Gumbel-max "
                         "T = 0.7, factor); batched (32 x 512 x 126464 bf16, strict threshold)")
@@ -91,26 +100,117 @@ def copy_probe():
     print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
 
 
-def cpu_baseline(w, logit_bytes, min_seconds):
-    """The oracle as it stands, on the same canvas, single process."""
+_CPU_W = None                     # the workload, inherited by the forked workers
+
+
+def _oracle_positions(chunk):
+    """The oracle's statistics at a list of (b, l) positions (a pool task)."""
+    import oracle
+    st = oracle.token_stats(_CPU_W.logits, "bf16", positions=chunk)
+    return [(b, l, int(st.x0[b, l]), float(st.prob[b, l]), float(st.entropy[b, l]))
+            for b, l in chunk]
+
+
+def _oracle_step(pool, chunks):
+    """One commit step of the oracle as it stands: statistics of every position
+    (spread over the pool's workers, or in this process), then entropy_bound
+    and edit on the whole canvas."""
     import numpy as np
     import oracle
+    w = _CPU_W
+    B, L, _ = w.shape
+    x0 = np.zeros((B, L), dtype=np.int32)
+    prob = np.zeros((B, L))
+    ent = np.zeros((B, L))
+    parts = pool.map(_oracle_positions, chunks) if pool is not None else \
+        [_oracle_positions(c) for c in chunks]
+    for part in parts:
+        for b, l, x, pr, en in part:
+            x0[b, l], prob[b, l], ent[b, l] = x, pr, en
     p = w.params
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        st = oracle.token_stats(w.logits, "bf16")
-        oracle.entropy_bound_transfer(st.entropy.astype(np.float32), w.cand, p["gamma"])
-        oracle.edit_transfer(st.x0, st.prob.astype(np.float32), w.tokens, w.editable, p["tau_edit"])
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= min_seconds:
-            break
+    oracle.entropy_bound_transfer(ent.astype(np.float32), w.cand, p["gamma"])
+    oracle.edit_transfer(x0, prob.astype(np.float32), w.tokens, w.editable, p["tau_edit"])
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(w, logit_bytes, min_seconds, max_workers=16):
+    """The oracle as it stands on the same canvas: a fork pool of one worker
+    per core this process may run on (at most max_workers, the host share of
+    one GPU), each computing the statistics of a share of the positions; the
+    rules run in the parent.  Timed again with one worker for comparison.
+    Must run before this process touches the GPU (the workers are forked)."""
+    import multiprocessing as mp
+    global _CPU_W
+    _CPU_W = w
     B, L, V = w.shape
+    affinity = len(os.sched_getaffinity(0))
+    workers = max(1, min(affinity, max_workers))
+    positions = [(b, l) for b in range(B) for l in range(L)]
+
+    def run(pool, n_chunks, seconds):
+        chunks = [positions[i::n_chunks] for i in range(n_chunks)]
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            _oracle_step(pool, chunks)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                return reps, el
+
+    reps1, el1 = run(None, 1, min_seconds / 2)
+    with mp.get_context("fork").Pool(workers) as pool:
+        _oracle_step(pool, [positions[i::workers] for i in range(workers)])     # start the workers
+        reps, el = run(pool, workers, min_seconds)
     return {"value": round(logit_bytes * reps / el / 1e9, 4), "unit": "GB/s",
-            "positions_per_s": round(B * L * reps / el, 2), "cores": 1, "kind": "oracle",
-            "seconds": round(el, 2),
+            "positions_per_s": round(B * L * reps / el, 2), "cores": workers, "kind": "oracle",
+            "seconds": round(el, 2), "cpu_model": _cpu_model(), "affinity_cpus": affinity,
+            "one_worker": {"value": round(logit_bytes * reps1 / el1 / 1e9, 4), "unit": "GB/s",
+                           "seconds": round(el1, 2), "repetitions": reps1},
             "sample": f"the full canvas ({B}x{L}x{V} bf16) with entropy_bound and edit, "
-                      f"{reps} repetition(s), numpy float64 oracle in one process"}
+                      f"{reps} repetition(s); numpy float64 oracle, statistics spread over "
+                      f"{workers} forked worker process(es), rules in the parent"}
+
+
+GROUP = 25         # back-to-back launches per pair of events in per_launch_us
+
+
+def per_launch_us(launch, groups):
+    """Device time per launch, as the mean over each of `groups` groups of
+    GROUP back-to-back launches, each group between its own pair of HIP
+    events on the launch stream (the current stream); returns the sorted
+    group means in microseconds.  (A pair of events around every single
+    launch adds the event packets' own time, a few microseconds, to each
+    launch; over a group it adds a fraction of one.)"""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(groups)]
+    for g in range(groups):
+        ev[g][0].record()
+        for i in range(GROUP):
+            launch(g * GROUP + i)
+        ev[g][1].record()
+    torch.cuda.synchronize()
+    return sorted(a.elapsed_time(b) * 1e3 / GROUP for a, b in ev)
+
+
+def launch_stats(us):
+    n = len(us)
+    med = us[n // 2] if n % 2 else 0.5 * (us[n // 2 - 1] + us[n // 2])
+    return {"median_us": round(med, 3), "mean_us": round(sum(us) / n, 3),
+            "p10_us": round(us[n // 10], 3), "p90_us": round(us[(9 * n) // 10], 3),
+            "groups": n, "group_size": GROUP,
+            "method": "median over the groups of each group's mean launch time; a group is "
+                      f"{GROUP} back-to-back launches between one pair of HIP events"}
 
 
 def llada_block_loop(args):
@@ -305,11 +405,19 @@ def fused_workload(args):
     if rc:
         raise RuntimeError(lib.dllm_last_error().decode())
     ms = start.elapsed_time(end) / steps
+
+    def one(i):
+        nonlocal rc
+        rc |= fn(*calls[i % len(calls)])
+    per = launch_stats(per_launch_us(one, max(20, steps // GROUP)))
+    if rc:
+        raise RuntimeError(lib.dllm_last_error().decode())
     logit_bytes = B * L * V * esz
     gbs = logit_bytes / (ms * 1e-3) / 1e9
     line = {
         "metric": "logit GB/s of the fused token_stats + rule launch", "value": round(gbs, 2),
         "unit": "GB/s", "n_gpus": 1, "steps": steps, "us_per_launch": round(ms * 1e3, 3),
+        "per_launch": per,
         "higher_is_better": True, "dtype": "bf16" if esz == 2 else "f32", "data": "synthetic",
         "pct_hbm_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
         "positions_per_s": round(B * L / (ms * 1e-3), 1),
@@ -388,6 +496,7 @@ def main():
     if args.workload in ("tiny", "dream_canvas", "batched"):
         fused_workload(args)
         return
+    fused = args.workload == "diffusiongemma_canvas"
 
     import numpy as np
     import torch
@@ -395,11 +504,17 @@ def main():
     import commit_step_amd as dc
     import workloads
 
-    torch.cuda.set_device(0)
-    dev = torch.device("cuda:0")
     w = workloads.config4()
     B, L, V = w.shape
     p = w.params
+    logit_bytes = B * L * V * 2
+    # the oracle's baseline first: its workers are forked before this process
+    # touches the GPU
+    cpu = None if args.no_cpu_baseline or not fused else \
+        cpu_baseline(w, logit_bytes, args.cpu_seconds)
+
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
     R = max(1, args.rotate)
     base = torch.from_numpy(w.logits.view(np.int16)).view(torch.bfloat16).to(dev)
     rot = torch.empty((R, B, L, V), dtype=torch.bfloat16, device=dev)
@@ -425,10 +540,13 @@ def main():
     rules[1].param, rules[1].tokens = p["tau_edit"], tokens.data_ptr()
     stream = torch.cuda.current_stream(dev).cuda_stream
     call_args = [(rot[i].data_ptr(), dc.DLLM_BF16, B, L, V, V, 0.0, 0, 0, None, 0,
-                  x0.data_ptr(), prob.data_ptr(), ent.data_ptr(), None, rules, 2, ws.data_ptr(),
-                  ws.numel(), stream) for i in range(R)]
+                  x0.data_ptr(), prob.data_ptr(), ent.data_ptr(), None, rules if fused else None,
+                  2 if fused else 0, ws.data_ptr(), ws.numel(), stream) for i in range(R)]
     fn = lib.dllm_token_stats
 
+    # the plain-read ceiling first: it also brings the GPU to its steady
+    # clocks, as a decode loop that runs one step after another keeps it
+    ceiling = read_ceiling(lib, rot, logit_bytes, B * L, stream, args.ceiling_launches)
     rc = 0
     for i in range(args.warmup):
         rc |= fn(*call_args[i % R])
@@ -449,11 +567,23 @@ def main():
     if rc:
         raise RuntimeError(lib.dllm_last_error().decode())
     ms = start.elapsed_time(end) / args.steps
+    # the launches again in groups between their own events: the median of
+    # the group means is the kernel's device time per launch, the roofline's
+    # denominator
+    rc = 0
 
-    logit_bytes = B * L * V * 2
-    per_position = 1 + 1 + 4 + 12 + 1 + 1        # cand, editable, tokens in; stats, masks out
+    def one(i):
+        nonlocal rc
+        rc |= fn(*call_args[i % R])
+    per = launch_stats(per_launch_us(one, max(20, args.steps // GROUP)))
+    if rc:
+        raise RuntimeError(lib.dllm_last_error().decode())
+    med_ms = per["median_us"] * 1e-3
+
+    # cand, editable, tokens in; stats, masks out (the statistics alone: stats out)
+    per_position = 1 + 1 + 4 + 12 + 1 + 1 if fused else 12
     alg_bytes = logit_bytes + B * L * per_position
-    achieved = alg_bytes / (ms * 1e-3) / 1e9
+    achieved = alg_bytes / (med_ms * 1e-3) / 1e9
     src_hash = kernel_source_hash()
     line = {
         "metric": "logit GB/s and positions/sec for token_stats+transfer; % of HBM peak",
@@ -469,31 +599,35 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "diffusiongemma_canvas: fused token_stats (greedy) + "
-                               "entropy_bound(gamma=0.5) + edit(tau=0.9)",
+                               "entropy_bound(gamma=0.5) + edit(tau=0.9)" if fused else
+                               "diffusiongemma_stats: token_stats (greedy), no rule",
                    "B": B, "L": L, "V": V, "logits": "bf16", "rotated_copies": R},
         "positions_per_s": round(B * L / (ms * 1e-3), 1),
         "steps_per_s": round(1e3 / ms, 1),
         "pct_hbm_peak": round(100.0 * achieved / HBM_PEAK_GBS, 2),
         "host_wall_ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "per_launch": per,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": read_traffic(src_hash),
-                     "kernel": "dllm::token_stats_kernel (bf16, greedy, 16-byte loads) with "
-                               "entropy_bound and edit fused",
+                     "time": "per_launch.median_us",
+                     "frac_event_mean": round(alg_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "kernel": "dllm::token_stats_kernel (bf16, greedy, 16-byte loads)" +
+                               (" with entropy_bound and edit fused" if fused else ""),
                      "algorithmic_bytes_per_launch": alg_bytes},
         "kernel_source_sha256": src_hash,
     }
-    line["read_ceiling"] = read_ceiling(lib, rot, logit_bytes, B * L, args, ms, stream)
-    line["cpu_baseline"] = None if args.no_cpu_baseline else \
-        cpu_baseline(w, logit_bytes, args.cpu_seconds)
+    ceiling["step_median_over_best_read"] = round(per["median_us"] / ceiling["best_us"], 3)
+    line["read_ceiling"] = ceiling
+    line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 
 
-def read_ceiling(lib, rot, logit_bytes, rows, args, ms, stream):
+def read_ceiling(lib, rot, logit_bytes, rows, stream, launches=2000):
     """A plain read of the same rotated logit copies (dllm_read_probe, the same
-    16-byte loads, no arithmetic), timed like the step: once with the step's
-    decomposition (one row per 512-thread workgroup) and once over 8 x 256
-    workgroups of 256 threads; the step's time as a fraction of the faster."""
+    16-byte loads, no arithmetic), timed with HIP events over `launches`
+    launches: once with the step's decomposition (one row per 512-thread
+    workgroup) and once over 8 x 256 workgroups of 256 threads."""
     import torch
 
     sink = torch.zeros(1, dtype=torch.int32, device=rot.device)
@@ -508,17 +642,17 @@ def read_ceiling(lib, rot, logit_bytes, rows, args, ms, stream):
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
-        for i in range(args.steps):
+        for i in range(launches):
             rc |= lib.dllm_read_probe(*args_i[i % len(args_i)])
         b.record()
         torch.cuda.synchronize()
         if rc:
             raise RuntimeError(lib.dllm_last_error().decode())
-        us = a.elapsed_time(b) / args.steps * 1e3
+        us = a.elapsed_time(b) / launches * 1e3
         res[name] = {"workgroups": wgs, "threads": nt, "us": round(us, 3),
                      "gb_s": round(logit_bytes / (us * 1e-6) / 1e9, 1)}
-    best = min(v["us"] for v in res.values())
-    res["step_time_over_best_read"] = round(ms * 1e3 / best, 3)
+    res["launches"] = launches
+    res["best_us"] = min(v["us"] for v in res.values() if isinstance(v, dict))
     return res
 
 

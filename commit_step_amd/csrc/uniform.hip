@@ -46,7 +46,8 @@ struct StopArgs {
   int64_t L;
   int k;                 // stability threshold
   int first;             // no previous canvas yet
-  int conf_class;        // 0: compare with thr, 1: always confident, 2: never
+  int conf_class;        // a finite sum: 0 compare with thr, 1 always confident, 2 never
+  int c_pinf;            // c = +inf (and L > 0): a +inf sum is confident too
   Fx thr;                // floor(c L 2^149)
   int32_t *prev;
   int32_t *count;
@@ -54,28 +55,35 @@ struct StopArgs {
 };
 
 // One workgroup per batch row: is the argmax canvas the previous one, and is
-// the exact sum of the entropies (fixed point, units of 2^-149) at most c L?
+// the sum of the entropies at most c L in the extended reals?  Finite terms
+// are summed exactly (fixed point, units of 2^-149); a NaN term, or +inf and
+// -inf together, leaves the sum undefined (not confident); +inf terms make it
+// +inf (confident only for c = +inf), -inf terms -inf (confident).
 template <int NT>
 __global__ __launch_bounds__(NT) void stop_kernel(StopArgs a) {
   __shared__ Fx s_sum[NT];
-  __shared__ int s_diff, s_bad;
+  __shared__ int s_diff, s_nan, s_pinf, s_ninf;
   const int tid = threadIdx.x;
   const int64_t base = (int64_t)blockIdx.x * a.L;
-  if (tid == 0) { s_diff = 0; s_bad = 0; }
+  if (tid == 0) { s_diff = 0; s_nan = 0; s_pinf = 0; s_ninf = 0; }
   __syncthreads();
   Fx acc;
   fx_zero(acc);
-  int diff = 0, bad = 0;
+  int diff = 0, nan = 0, pinf = 0, ninf = 0;
   for (int64_t l = tid; l < a.L; l += NT) {
     const int32_t am = a.argmax[base + l];
     if (!a.first && a.prev[base + l] != am) diff = 1;
     a.prev[base + l] = am;
     const uint32_t u = __float_as_uint(a.entropy[base + l]);
-    if (!bits_finite(u)) bad = 1;
-    else fx_add(acc, fx_from_f32_bits(u));
+    if (bits_finite(u)) fx_add(acc, fx_from_f32_bits(u));
+    else if (u & 0x007fffffu) nan = 1;
+    else if (u >> 31) ninf = 1;
+    else pinf = 1;
   }
   if (diff) s_diff = 1;
-  if (bad) s_bad = 1;
+  if (nan) s_nan = 1;
+  if (pinf) s_pinf = 1;
+  if (ninf) s_ninf = 1;
   s_sum[tid] = acc;
   __syncthreads();
   if (tid == 0) {
@@ -84,12 +92,18 @@ __global__ __launch_bounds__(NT) void stop_kernel(StopArgs a) {
     const bool same = !a.first && !s_diff;
     const int cnt = same ? a.count[blockIdx.x] + 1 : 0;
     a.count[blockIdx.x] = cnt;
-    const bool confident = !s_bad && (a.conf_class == 1 || (a.conf_class == 0 && fx_le(tot, a.thr)));
+    bool confident;
+    if (s_nan || (s_pinf && s_ninf)) confident = false;
+    else if (s_pinf) confident = a.c_pinf != 0;
+    else if (s_ninf) confident = true;
+    else confident = a.conf_class == 1 || (a.conf_class == 0 && fx_le(tot, a.thr));
     if (cnt >= a.k && confident) a.done[blockIdx.x] = 1;
   }
 }
 
-// floor(c * L * 2^149) as a signed 320-bit number, for |c| L < 2^141.
+// floor(c * L * 2^149) as a signed 320-bit number, for |c| L < 2^170 (the
+// product is mant L 2^(e-53) with mant < 2^53, L < 2^32: placed limb by limb,
+// it stays below the sign bit, 2^319).
 Fx fixed_floor_of_product(double c, uint32_t L) {
   Fx r;
   fx_zero(r);
@@ -202,12 +216,14 @@ extern "C" int dllm_stable_confident_stop(const int32_t *argmax, const float *en
   a.prev = prev_argmax;
   a.count = stable_steps;
   a.done = done;
-  // exact c L in fixed point; beyond +-2^141 the comparison is decided by sign
-  // (a sum of L finite float32 values stays below 2^160 in magnitude)
+  // exact c L in fixed point; from |c L| >= 2^160 on, the comparison with a
+  // finite sum is decided by the sign of c (L finite float32 values, each
+  // below 2^128, sum to less than 2^160 in magnitude)
   const double mag = fabs(confidence_threshold) * (double)(L > 0 ? L : 1);
   if (confidence_threshold == 0.0 || L == 0) a.conf_class = 0;
-  else if (mag >= 0x1p141 || confidence_threshold == INFINITY || confidence_threshold == -INFINITY)
+  else if (mag >= 0x1p160 || confidence_threshold == INFINITY || confidence_threshold == -INFINITY)
     a.conf_class = confidence_threshold > 0 ? 1 : 2;
+  a.c_pinf = (L > 0 && confidence_threshold == INFINITY) ? 1 : 0;
   if (a.conf_class == 0) a.thr = fixed_floor_of_product(confidence_threshold, (uint32_t)L);
   stop_kernel<256><<<dim3((unsigned)B), dim3(256), 0, stream>>>(a);
   return check_launch(who);

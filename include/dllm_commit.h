@@ -360,8 +360,10 @@ int dllm_renoise(const int32_t *sample, const uint8_t *accepted,
 /* StableConfidentStopping: per batch row, stable_steps[b] counts the
  * consecutive calls whose argmax row equals the previous call's (0 on the
  * first call, first != 0); the row is confident when the mean of its L
- * entropies is at most confidence_threshold (exact: sum <= c L, no rounding;
- * a non-finite entropy is never confident); done[b] |= (stable_steps[b] >=
+ * entropies is at most confidence_threshold (sum <= c L in the extended
+ * reals, finite terms summed exactly: a NaN, or +inf with -inf, is never
+ * confident; a +inf term only for c = +inf; a -inf term always; L = 0
+ * compares 0 with 0); done[b] |= (stable_steps[b] >=
  * stability_threshold && confident).  prev_argmax (B, L) int32 and
  * stable_steps (B,) int32 are the caller's state, updated in place; done (B,)
  * uint8 in/out.  stability_threshold >= 0, confidence_threshold not NaN. */

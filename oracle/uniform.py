@@ -90,14 +90,31 @@ class StableConfidentStopping:
             same = self.prev is not None and bool(np.array_equal(argmax[b], self.prev[b]))
             self.count[b] = self.count[b] + 1 if same else 0
             hs = np.asarray(entropy, dtype=np.float32)[b]
-            if not np.isfinite(hs).all():
-                confident = False                  # a non-finite entropy is never confident
-            else:
-                total = sum((Fraction(float(h)) for h in hs), Fraction(0))
-                confident = total <= Fraction(self.c) * L
-            done[b] = self.count[b] >= self.k and confident
+            done[b] = self.count[b] >= self.k and self._confident(hs)
         self.prev = argmax.copy()
         return done
+
+    def _confident(self, hs):
+        """mean(hs) <= c, i.e. sum(hs) <= c L, in the extended reals: the sum
+        is undefined (never confident) with a NaN or with both infinities, +inf
+        with a +inf term, -inf with a -inf term, else the exact rational sum.
+        An empty row sums to 0 and compares with 0 (its c L)."""
+        L = len(hs)
+        c = self.c
+        if L == 0:
+            return True
+        nan, pinf, ninf = bool(np.isnan(hs).any()), bool((hs == np.inf).any()), \
+            bool((hs == -np.inf).any())
+        if nan or (pinf and ninf):
+            return False
+        if pinf:
+            return c == np.inf                     # +inf <= c L only for c L = +inf
+        if ninf:
+            return True                            # -inf <= every c L
+        if np.isinf(c):
+            return c > 0                           # a finite sum against +-inf
+        total = sum((Fraction(float(h)) for h in hs), Fraction(0))
+        return total <= Fraction(c) * L
 
 
 def decode_uniform(model, B, L, V, seed, num_steps=48, entropy_bound=0.1, t_min=0.4, t_max=0.8,

@@ -26,7 +26,7 @@ pytestmark = pytest.mark.gpu
     ("f32", 2, 2, 131072 + 4, ()),                 # split rows, fp32
     ("bf16", 1, 2, 262144, ()),                    # split rows, largest V
     ("bf16", 4, 70, 32768, (7, 32767)),            # many rows, 256-thread groups
-    ("f32", 1, 300, 20000, ()),                    # 1024-thread groups
+    ("f32", 1, 300, 20000, ()),                    # 512-thread groups, one row each
 ])
 def test_greedy_parity(dtype, B, L, V, sup):
     bits, _ = random_logits(100 + V % 97, B, L, V, dtype, 2.5, 0.4, 4.0, 16.0, sup)

@@ -73,7 +73,9 @@ def test_stop_rule_matches_the_oracle_call_by_call():
                 am[rng.integers(B), rng.integers(L)] += 1       # a change restarts the count
             h = (rng.random((B, L)) * 0.5 * c if c > 0 else rng.random((B, L))).astype(np.float32)
             h[0] = np.float32(c) if c > 0 else 0.0              # the mean exactly at the bound
-            h[1, :2] = [np.inf, 0.0]                              # never confident
+            h[1, :2] = [np.inf, 0.0]                              # +inf: above a finite bound
+            h[3, :2] = [-np.inf, 1.0] if call % 2 else [-np.inf, np.inf]   # -inf / undefined
+            h[4, 0] = np.nan if call == 3 else h[4, 0]
             if L > 2 and c > 0:
                 h[2] = np.float32(c)
                 h[2, 0] = np.nextafter(np.float32(c), np.float32(10))   # a hair above
@@ -81,6 +83,25 @@ def test_stop_rule_matches_the_oracle_call_by_call():
             done_o |= o(am, h)
             assert np.array_equal(d, done_o), (k, c, call)
     log("stop rule: call-by-call parity")
+
+
+def test_stop_rule_infinite_and_large_bounds():
+    """c = +-inf and a bound c L between 2^141 and 2^160, against the oracle."""
+    L = 16384
+    rows = np.zeros((6, L), dtype=np.float32)
+    rows[0] = 3.4e38                                    # sum ~2^142
+    rows[1] = 1.0
+    rows[2, 0] = np.inf
+    rows[3, 0] = -np.inf
+    rows[4, :2] = [np.inf, -np.inf]
+    rows[5] = -2.0
+    am = np.zeros((6, L), dtype=np.int32)
+    for c in (1.5e38, 4e38, np.inf, -np.inf, 0.5, -1.0):
+        g = dc.StableConfidentStopping(0, c)
+        o = oracle.StableConfidentStopping(0, c)
+        d = g(torch.from_numpy(am).cuda(), torch.from_numpy(rows).cuda()).cpu().numpy()
+        assert np.array_equal(d, o(am, rows)), (c, d)
+    log("stop rule: infinite and large bounds")
 
 
 def _stand_in_model(B, L, V, target):

@@ -60,8 +60,10 @@ MUTATIONS = [
     ("uniform.py", "out[b, l] = (x * int(V)) >> 64", "out[b, l] = x % int(V)", "uniform_canvas"),
     ("uniform.py", "self.count[b] = self.count[b] + 1 if same else 0",
      "self.count[b] = self.count[b] + 1", "stopping"),
-    ("uniform.py", "confident = total <= Fraction(self.c) * L", "confident = total <= Fraction(self.c)",
-     "stopping"),
+    ("uniform.py", "return total <= Fraction(c) * L", "return total <= Fraction(c)", "stopping"),
+    ("uniform.py", "return True                            # -inf <= every c L",
+     "return False                           # -inf <= every c L", "extended_reals"),
+    ("uniform.py", "if nan or (pinf and ninf):", "if nan:", "extended_reals"),
     ("uniform.py", "canvas = np.where(done[:, None], canvas, new_canvas)", "canvas = new_canvas",
      "freezes_finished"),
     ("step.py", "take = (commit is not None and commit[b, l]) or (edit is not None and edit[b, l])",

@@ -103,7 +103,52 @@ def test_stable_confident_stopping_counts_and_exact_mean():
     zero = oracle.StableConfidentStopping(0, 0.1)
     assert zero(a, np.zeros((2, 2), np.float32)).tolist() == [True, True]
     h3 = np.array([[np.inf, 0.0], [np.nan, 0.0]], np.float32)
-    assert zero(a, h3).tolist() == [False, False]         # non-finite: never confident
+    assert zero(a, h3).tolist() == [False, False]         # +inf > c L; NaN compares false
+
+
+def _confident(c, row):
+    """One stable row through the oracle's rule (k = 0), as a bool."""
+    stop = oracle.StableConfidentStopping(0, c)
+    row = np.asarray(row, dtype=np.float32)
+    return bool(stop(np.zeros((1, len(row)), np.int32), row[None, :])[0])
+
+
+def test_stable_confident_stopping_extended_reals():
+    """The mean bound sum(H) <= c L taken in the extended reals, as IEEE
+    arithmetic evaluates it: sum and compare in float64 wherever float64 is
+    exact for the values used."""
+    inf, nan = np.inf, np.nan
+    cases = [
+        (0.1, [-inf, 5.0], True),          # -inf sum is below every bound
+        (-inf, [-inf, 5.0], True),         # -inf <= -inf
+        (0.1, [-inf, inf], False),         # -inf + inf is undefined
+        (inf, [-inf, inf], False),         # ... also against an infinite bound
+        (0.1, [-inf, nan], False),
+        (0.1, [inf, 0.0], False),          # +inf above a finite bound
+        (inf, [inf, 0.0], True),           # +inf <= +inf
+        (inf, [1e30, 3e38], True),         # a finite sum below +inf
+        (-inf, [-1e30, -3e38], False),     # a finite sum above -inf
+        (inf, [nan, 0.0], False),
+        (-0.5, [-0.5, -0.5], True),        # a negative bound met exactly
+        (-0.5, [-0.5, np.nextafter(np.float32(-0.5), np.float32(0))], False),
+    ]
+    for c, row, want in cases:
+        with np.errstate(invalid="ignore"):
+            s = float(np.sum(np.asarray(row, dtype=np.float64)))
+        assert (s <= c * len(row)) == want, (c, row)      # the IEEE evaluation agrees
+        assert _confident(c, row) == want, (c, row)
+
+
+def test_stable_confident_stopping_large_bound_is_exact():
+    """A bound c L of 2^141 to 2^160 still compares exactly: 16384 entropies
+    of 3.4e38 sum to ~5.6e42 (2^142.0), above c L = 1.5e38 x 16384 (2^141.2)
+    and below 4e38 x 16384; float64 holds both sides well apart."""
+    row = np.full(16384, 3.4e38, dtype=np.float32)
+    total = float(np.sum(row.astype(np.float64)))
+    assert total > 1.5e38 * 16384 and total < 4e38 * 16384
+    assert _confident(1.5e38, row) is False
+    assert _confident(4e38, row) is True
+    assert _confident(float(np.float32(3.4e38)), row) is True      # the mean exactly at c
 
 
 def test_uniform_loop_converges_to_the_models_canvas_and_freezes_rows():
