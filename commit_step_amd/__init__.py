@@ -67,6 +67,9 @@ _SIGNATURES = {
     "dllm_commit_step": (_I32, [_P, _I32, _I64, _I64, _I64, _I64, ctypes.c_float, ctypes.c_uint64,
                                 ctypes.c_uint64, _P, _I32, _P, _P, _P, _P, _P, _I32, _P, _P,
                                 ctypes.c_size_t, _P]),
+    "dllm_commit_step_static": (_I32, [_P, _I32, _I64, _I64, _I64, _I64, ctypes.c_float,
+                                       ctypes.c_uint64, ctypes.c_uint64, _P, _I32, _P, _P, _P, _P,
+                                       _P, _I32, _P, _P]),
     "dllm_transfer_threshold": (_I32, [_P, _P, _I64, _I64, ctypes.c_double, _I32, _P, _P]),
     "dllm_transfer_threshold_rows": (_I32, [_P, _P, _P, _I64, _I64, _I32, _P, _P]),
     "dllm_decaying_threshold": (_I32, [ctypes.c_double, ctypes.c_double, ctypes.c_double, _I64,
@@ -156,6 +159,10 @@ def _ws_size(dt, B, L, V, device):
     return n
 
 
+# commit_step(..., workspace=STATIC_WORKSPACE) runs dllm_commit_step_static: no
+# workspace tensor, no allocation (the library's own per-GPU array; calls that
+# overlap on one GPU race).
+STATIC_WORKSPACE = "static"
 _MASK_DTYPES = (torch.bool, torch.uint8)
 _workspaces = {}
 
@@ -293,6 +300,10 @@ def commit_step(logits, tokens, rules, temperature=0.0, seed=None, step=0, suppr
     read (their x0 / prob / entropy are left as they were).  ``counts`` (True,
     or a preallocated (B, 2) int32 tensor, device or pinned host) receives per
     batch row the candidates left uncommitted and the positions edited.
+    ``workspace``: None (the stream's default buffer), a zero-filled uint8
+    tensor of workspace_size() bytes, or STATIC_WORKSPACE (the library's own
+    per-GPU array, no allocation; shapes up to DLLM_STATIC_SCRATCH_BYTES of
+    workspace; calls that overlap on one GPU race).
     Returns CommitStep(stats, counts).
     """
     B, L = logits.shape[0], logits.shape[1]
@@ -375,13 +386,19 @@ def _stats_call(logits, temperature, seed, step, suppress_ids, rules, out, works
     dt = DLLM_BF16 if logits.dtype == torch.bfloat16 else DLLM_F32
     lib = load_library()
     with _on(dev):
-        need = _ws_size(dt, B, L, V, dev)
         stream = _stream(logits)
-        ws = workspace if workspace is not None else _workspace(dev, stream, need)
         args = [logits.data_ptr(), dt, B, L, V, row_stride, float(temperature),
                 int(seed or 0) & 0xFFFFFFFFFFFFFFFF, int(step), sup, len(suppress_ids),
                 x0.data_ptr(), prob.data_ptr(), ent.data_ptr(), ctypes.byref(extra),
                 crules if len(rules) else None, len(rules)]
+        if isinstance(workspace, str):
+            if workspace != STATIC_WORKSPACE or canvas is None:
+                raise ValueError("workspace='static' is taken by commit_step only")
+            _check(lib.dllm_commit_step_static(*args, ctypes.byref(canvas[0]), stream),
+                   "dllm_commit_step_static")
+            return Stats(x0, prob, ent, mar, am)
+        need = _ws_size(dt, B, L, V, dev)
+        ws = workspace if workspace is not None else _workspace(dev, stream, need)
         if canvas is None:
             _check(lib.dllm_token_stats(*args, ws.data_ptr(), ws.numel(), stream),
                    "dllm_token_stats")

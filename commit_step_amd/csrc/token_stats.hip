@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "token_stats_dev.h"
 
@@ -262,4 +263,80 @@ extern "C" int dllm_commit_step(const void *logits, int dtype, int64_t B, int64_
   return stats_step("dllm_commit_step", logits, dtype, B, L, V, row_stride, temperature, seed,
                     step, suppress_ids, n_suppress, x0, prob, entropy, extra, rules, n_rules,
                     canvas, workspace, workspace_bytes, stream);
+}
+
+namespace dllm {
+namespace {
+
+// The workspace of dllm_commit_step_static: one array on each GPU, part of the
+// code object (zero-initialised static storage).  In host code this name is a
+// host-side stand-in, not the device address: kernels get the address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[DLLM_STATIC_SCRATCH_BYTES];
+
+__global__ void clear_scratch_kernel(uint4 *p, size_t n16) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+struct ScratchSlot {
+  void *ptr = nullptr;    // device address of `scratch` on this device
+  bool cleared = false;
+};
+std::mutex g_scratch_mu;
+ScratchSlot g_scratch[64];
+
+// The current device's scratch address.  Once per device: the symbol lookup
+// (with that device current) and one clearing kernel on `stream`.
+int static_scratch(hipStream_t stream, void **out, const char *who) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+    return fail(DLLM_ERR_HIP, "%s: no current device", who);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  ScratchSlot &slot = g_scratch[dev];
+  if (!slot.ptr) {
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(DLLM_ERR_HIP, "%s: hipGetSymbolAddress(scratch) failed: %s", who,
+                  hipGetErrorString(e));
+    slot.ptr = p;
+  }
+  if (!slot.cleared) {
+    clear_scratch_kernel<<<dim3(256), dim3(256), 0, stream>>>(static_cast<uint4 *>(slot.ptr),
+                                                              DLLM_STATIC_SCRATCH_BYTES / 16);
+    const int rc = check_launch(who);
+    if (rc != DLLM_OK) return rc;
+    slot.cleared = true;
+  }
+  *out = slot.ptr;
+  return DLLM_OK;
+}
+
+}  // namespace
+}  // namespace dllm
+
+extern "C" int dllm_commit_step_static(const void *logits, int dtype, int64_t B, int64_t L,
+                                       int64_t V, int64_t row_stride, float temperature,
+                                       uint64_t seed, uint64_t step,
+                                       const int32_t *suppress_ids, int n_suppress, int32_t *x0,
+                                       float *prob, float *entropy,
+                                       const dllm_stats_extra *extra, const dllm_rule *rules,
+                                       int n_rules, const dllm_canvas *canvas,
+                                       hipStream_t stream) {
+  const char *who = "dllm_commit_step_static";
+  if (!canvas) return fail(DLLM_ERR_ARG, "%s: canvas is NULL", who);
+  const size_t need = dllm_token_stats_workspace_size(dtype, B, L, V);
+  if (need > DLLM_STATIC_SCRATCH_BYTES)
+    return fail(DLLM_ERR_UNSUPPORTED,
+                "%s: this shape needs %zu bytes of workspace, more than the %u of the static "
+                "scratch array; call dllm_commit_step with a workspace", who, need,
+                (unsigned)DLLM_STATIC_SCRATCH_BYTES);
+  void *ws = nullptr;
+  const int rc = static_scratch(stream, &ws, who);
+  if (rc != DLLM_OK) return rc;
+  return stats_step(who, logits, dtype, B, L, V, row_stride, temperature, seed, step,
+                    suppress_ids, n_suppress, x0, prob, entropy, extra, rules, n_rules, canvas,
+                    ws, DLLM_STATIC_SCRATCH_BYTES, stream);
 }

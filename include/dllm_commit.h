@@ -60,6 +60,8 @@ enum { DLLM_F32 = 0, DLLM_BF16 = 1 };
 
 #define DLLM_MAX_L 4096
 #define DLLM_MAX_SUPPRESS 64
+/* bytes of the library-owned workspace of dllm_commit_step_static, per GPU */
+#define DLLM_STATIC_SCRATCH_BYTES (1u << 20)
 
 enum {
   DLLM_RULE_THRESHOLD = 1,
@@ -237,6 +239,30 @@ int dllm_commit_step(const void *logits, int dtype, int64_t B, int64_t L,
                      const dllm_canvas *canvas,
                      void *workspace, size_t workspace_bytes,
                      hipStream_t stream);
+
+/* dllm_commit_step with no workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops and
+ * harnesses that forbid hipMalloc).  It allocates nothing: the counters and
+ * split-row partials live in a library-owned device array of
+ * DLLM_STATIC_SCRATCH_BYTES on each GPU, part of the library's code object
+ * and held until the process ends.  Arguments, layouts and errors are those
+ * of dllm_commit_step, plus DLLM_ERR_UNSUPPORTED when the shape needs more
+ * than DLLM_STATIC_SCRATCH_BYTES (the need is
+ * dllm_token_stats_workspace_size(dtype, B, L, V)), checked before anything
+ * is launched.  Every call on one GPU shares that GPU's array: calls that can
+ * overlap (issued on two streams, or from two host threads without ordering)
+ * race and give wrong results; calls on one stream are ordered and safe.
+ * Each call leaves the array zero-filled, which the next call needs; the
+ * first call on a device also clears it once, with one small kernel on
+ * `stream`. */
+int dllm_commit_step_static(const void *logits, int dtype, int64_t B, int64_t L,
+                            int64_t V, int64_t row_stride, float temperature,
+                            uint64_t seed, uint64_t step,
+                            const int32_t *suppress_ids, int n_suppress,
+                            int32_t *x0, float *prob, float *entropy,
+                            const dllm_stats_extra *extra,
+                            const dllm_rule *rules, int n_rules,
+                            const dllm_canvas *canvas, hipStream_t stream);
 
 /* threshold_transfer ("What mlx-arsenal ships", threshold_transfer row; mlxcel
  * "Block Diffusion", "LLaDA-2 Block Unmasking"): per batch row, commit every

@@ -141,6 +141,24 @@ def test_commit_step_argument_errors(lib):
     assert call(ctypes.byref(cv), B=0) == 0
 
 
+def test_commit_step_static_host_checks(lib):
+    """The allocation-free entry point checks its canvas and the static
+    array's size on the host, before any device call."""
+    import commit_step_amd as dc
+    P = ctypes.c_void_p
+    fake = P(16)
+    cv = dc._CCanvas()
+
+    def call(canvas, B, L, V):
+        return lib.dllm_commit_step_static(fake, 1, B, L, V, V, 0.0, 0, 0, None, 0, fake, P(24),
+                                           P(40), None, None, 0, canvas, None)
+
+    assert call(None, 1, 4, 8) == -1 and "canvas" in _err(lib)
+    B, L, V = 300000, 1, 64
+    assert lib.dllm_token_stats_workspace_size(1, B, L, V) > (1 << 20)
+    assert call(ctypes.byref(cv), B, L, V) == -5 and "static" in _err(lib)
+
+
 def test_uniform_helpers_argument_errors(lib):
     import commit_step_amd as dc
     P = ctypes.c_void_p
