@@ -88,6 +88,7 @@ _SIGNATURES = {
     "dllm_stable_confident_stop": (_I32, [_P, _P, _I64, _I64, _I32, ctypes.c_double, _I32, _P, _P,
                                           _P, _P]),
     "dllm_read_probe": (_I32, [_P, _I64, _I64, _I32, _P, _P]),
+    "dllm_stage_timestamps": (_I32, [_P, ctypes.c_size_t, _I32]),
     "dllm_last_error": (ctypes.c_char_p, []),
 }
 
@@ -96,18 +97,35 @@ def library_path():
     return _LIB_PATH
 
 
-def load_library():
-    """Load libdllm_commit.so (raises if it has not been built)."""
-    global _lib
+_STAGES_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdllm_commit_stages.so")
+_lib_stages = None
+
+
+def _open(path):
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+def load_library(stages=False):
+    """Load libdllm_commit.so (raises if it has not been built).  stages=True
+    loads libdllm_commit_stages.so instead, the same library with stage
+    timestamps on (for commit_step_amd.stage_timing only)."""
+    global _lib, _lib_stages
+    if stages:
+        if _lib_stages is None:
+            if not os.path.exists(_STAGES_PATH):
+                raise RuntimeError(f"{_STAGES_PATH} is not built; run "
+                                   "`python -m commit_step_amd.build --stages`")
+            _lib_stages = _open(_STAGES_PATH)
+        return _lib_stages
     if _lib is None:
         if not os.path.exists(_LIB_PATH):
             raise RuntimeError(f"{_LIB_PATH} is not built; run `python -m commit_step_amd.build`")
-        lib = ctypes.CDLL(_LIB_PATH)
-        for name, (res, args) in _SIGNATURES.items():
-            fn = getattr(lib, name)
-            fn.restype = res
-            fn.argtypes = args
-        _lib = lib
+        _lib = _open(_LIB_PATH)
     return _lib
 
 

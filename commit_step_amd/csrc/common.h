@@ -25,6 +25,71 @@ int device_cu_count();
 // queried; else DLLM_OK.
 int check_lds(const void *kernel, size_t dynamic_lds, const char *who);
 
+// Stage timestamps (an instrumented build only, -DDLLM_STAGE_TIMESTAMPS):
+// thread 0 of each workgroup records the 100 MHz real-time counter when it
+// reaches a stage of the step, in LDS (an LDS write adds no wait for memory
+// to the step it measures), and copies the records to a device array of
+// this translation unit when the kernel returns (the first kStageWorkgroups
+// workgroups), which dllm_stage_timestamps copies out.  A kernel opts in with
+// DLLM_STAGE_SCOPE() at its start.  In the product build these are empty.
+constexpr int kStageWorkgroups = 4096;
+constexpr int kStages = 16;
+enum Stage {
+  kStageStart = 0,         // first instruction
+  kStageStreamEnd = 1,     // the slice streamed and its waves merged
+  kStageSliceCounted = 2,  // split rows: the slice partial published and counted
+  kStageRowMerged = 3,     // split rows, last slice: every slice merged
+  kStagePublished = 4,     // the row's statistics written
+  kStageBatchCounted = 5,  // the row counted into its batch row
+  kStageBatchDone = 6,     // the completing workgroup: rules and counts done
+  kStageSkipped = 7,       // canvas step: the row needed by no rule, not read
+  kStageFinalized = 8,     // the row's statistics computed (before they are written)
+  kStageStoresDrained = 9, // the row's stores complete, before its batch-row count
+  kStageRuleLoaded = 10,   // the completing workgroup: the rule's inputs loaded
+  kStageRuleRanked = 11,   // the completing workgroup: the candidates ranked
+};
+#ifdef DLLM_STAGE_TIMESTAMPS
+static __device__ uint64_t stage_ts[kStageWorkgroups * kStages];
+static __shared__ uint64_t stage_lds[kStages];
+// The counter read waits for itself in the same asm block, and the memory
+// clobber keeps the compiler from moving memory operations across a stage mark.
+__device__ __forceinline__ uint64_t stage_clock() {
+  uint64_t t;
+  asm volatile("s_memrealtime %0\n\ts_waitcnt lgkmcnt(0)" : "=s"(t) : : "memory");
+  return t;
+}
+#define DLLM_STAGE(k)                                                                     \
+  do {                                                                                    \
+    if (threadIdx.x == 0) stage_lds[(k)] = stage_clock();                                 \
+  } while (0)
+struct StageFlush {
+  __device__ StageFlush() {
+    if (threadIdx.x == 0)
+      for (int k = 0; k < kStages; ++k) stage_lds[k] = 0;
+  }
+  __device__ ~StageFlush() {
+    // stages this workgroup did not pass keep their older records
+    if (threadIdx.x == 0 && blockIdx.x < (unsigned)kStageWorkgroups)
+      for (int k = 0; k < kStages; ++k)
+        if (stage_lds[k]) stage_ts[blockIdx.x * kStages + k] = stage_lds[k];
+  }
+};
+#define DLLM_STAGE_SCOPE() StageFlush stage_flush_
+// Copies this translation unit's array to host memory (clear: zero it first
+// instead); hipMemcpy*Symbol status.
+hipError_t stage_ts_copy_full(uint64_t *dst, bool clear);
+hipError_t stage_ts_copy_plain(uint64_t *dst, bool clear);
+#define DLLM_STAGE_COPY_IMPL(name)                                                        \
+  hipError_t name(uint64_t *dst, bool clear) {                                            \
+    static uint64_t zeros[kStageWorkgroups * kStages];                                    \
+    if (clear) return hipMemcpyToSymbol(HIP_SYMBOL(stage_ts), zeros, sizeof(zeros));      \
+    return hipMemcpyFromSymbol(dst, HIP_SYMBOL(stage_ts), sizeof(zeros));                 \
+  }
+#else
+#define DLLM_STAGE(k) do { } while (0)
+#define DLLM_STAGE_SCOPE() do { } while (0)
+#endif
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.69314718055994531f;
 

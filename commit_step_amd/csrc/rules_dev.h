@@ -493,6 +493,7 @@ __device__ inline bool short_entropy_rule(const RuleDev &r, int b, int L, const 
     anybad |= wA[w] >> 20;
     nxt = wNext[w] < nxt ? wNext[w] : nxt;
   }
+  DLLM_STAGE(kStageRuleLoaded);
   if (anybad || nF + 1 > nt || nF > 1024) return false;
   const int nc = nF + nA;
   if (in_f) {
@@ -538,6 +539,7 @@ __device__ inline bool short_entropy_rule(const RuleDev &r, int b, int L, const 
     }
     const int ns1 = first1 != 0x7fffffff ? first1 : min(nF + 1, nc);
     const int ncm1 = nc ? max(ns1, 1) : 0;
+    DLLM_STAGE(kStageRuleRanked);
     if (lv) {
       const bool c1 = rk < ncm1;
       o_row[(uint32_t)qk] = c1 ? 1 : 0;

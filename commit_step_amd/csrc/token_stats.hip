@@ -73,6 +73,37 @@ int prepare_rule(const dllm_rule &r, RuleDev &d, int64_t B, int64_t L, const cha
 
 using namespace dllm;
 
+#ifdef DLLM_STAGE_TIMESTAMPS
+namespace dllm {
+DLLM_STAGE_COPY_IMPL(stage_ts_copy_plain)
+}  // namespace dllm
+#endif
+
+extern "C" int dllm_stage_timestamps(uint64_t *dst, size_t n, int clear) {
+#ifdef DLLM_STAGE_TIMESTAMPS
+  const size_t slots = (size_t)kStageWorkgroups * kStages;
+  if (clear) {
+    if (stage_ts_copy_plain(nullptr, true) != hipSuccess ||
+        stage_ts_copy_full(nullptr, true) != hipSuccess)
+      return fail(DLLM_ERR_HIP, "dllm_stage_timestamps: clearing failed");
+    return ok();
+  }
+  if (!dst || n < slots)
+    return fail(DLLM_ERR_ARG, "dllm_stage_timestamps: dst needs %zu slots", slots);
+  static uint64_t other[(size_t)kStageWorkgroups * kStages];
+  if (stage_ts_copy_plain(dst, false) != hipSuccess ||
+      stage_ts_copy_full(other, false) != hipSuccess)
+    return fail(DLLM_ERR_HIP, "dllm_stage_timestamps: copy failed");
+  for (size_t i = 0; i < slots; ++i)           // one of the two kernel families ran
+    if (other[i]) dst[i] = other[i];
+  return ok();
+#else
+  (void)dst; (void)n; (void)clear;
+  return fail(DLLM_ERR_UNSUPPORTED,
+              "dllm_stage_timestamps: the library was built without stage timestamps");
+#endif
+}
+
 extern "C" size_t dllm_token_stats_workspace_size(int dtype, int64_t B, int64_t L, int64_t V) {
   if ((dtype != DLLM_F32 && dtype != DLLM_BF16) || B < 0 || L < 0 || V < 1) return 0;
   const Plan p = make_plan(dtype, B * L, V, V, nullptr);

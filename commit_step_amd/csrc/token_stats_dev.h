@@ -54,6 +54,8 @@ constexpr int kIdxNone = 0x7fffffff;
 constexpr int kMaxRules = 2;
 constexpr int kMaxSlices = 256;   // slices of one row (partials merged in LDS)
 
+
+
 struct Partial {          // one row slice's statistics (workspace)
   float M;                // max of the slice (-inf: empty)
   int idx;                // first index of M
@@ -808,9 +810,26 @@ __device__ __forceinline__ bool row_needed(const StatsArgs &a, int64_t row_id) {
   return need != 0;
 }
 
-// Statistics of a finished row from its merged partial; false when the row is
-// degenerate (NaN, +inf, or no finite unsuppressed logit) and needs the
-// two-pass path.
+// log(1 + z) for finite z >= 0 in a few instructions: with u = RN(1 + z),
+// log1p(z) = log(u) z / (u - 1), which keeps the relative accuracy of log(u)
+// however small z is (D. Goldberg, "What every computer scientist should know
+// about floating-point arithmetic", ACM Computing Surveys 23(1), 1991,
+// Theorem 4); log(u) from the hardware base-2 logarithm (1 ulp) and the
+// quotient from the hardware reciprocal (1 ulp): a few ulp in all.
+__device__ __forceinline__ float log1p_nonneg(float z) {
+  const float u = 1.0f + z;
+  const float um1 = u - 1.0f;
+  if (um1 == 0.0f) return z;
+  return __builtin_amdgcn_logf(u) * kLn2 * (z * __builtin_amdgcn_rcpf(um1));
+}
+
+// The row's statistics from its merged partial; false for a degenerate row
+// (NaN, +inf, no finite unsuppressed logit), which slow_row recomputes.  One
+// thread runs this on the critical path after the slowest row's stream, so it
+// uses the hardware reciprocal and logarithm (a few ulp) instead of the
+// correctly rounded division and the library log1p (~150 dependent
+// instructions).  z >= 0 and S <= 0 (every d <= 0), so H = log1p(z) - ln2 S /
+// (1 + z) adds two non-negative terms and keeps their relative accuracy.
 template <bool SAMPLE, bool FULL>
 __device__ __forceinline__ bool finalize_partial(const Partial &p, float c, RowResult &res) {
   const bool ok = bits_finite(__float_as_uint(p.M)) && bits_finite(__float_as_uint(p.z)) &&
@@ -818,16 +837,17 @@ __device__ __forceinline__ bool finalize_partial(const Partial &p, float c, RowR
                   (!SAMPLE || (p.ib != kIdxNone && bits_finite(__float_as_uint(p.sb))));
   if (ok) {
     const float zf = 1.0f + p.z;
-    res.ent = log1pf(p.z) - kLn2 * p.S / zf;
+    const float rz = __builtin_amdgcn_rcpf(zf);
+    res.ent = log1p_nonneg(p.z) - kLn2 * p.S * rz;
     // (1 - e^((runner-up - max)/Ts)) / z; only the FULL kernels track the runner-up
-    res.margin = FULL ? -expm1f((p.R2 - p.M) * c * kLn2) / zf : 0.f;
+    res.margin = FULL ? -expm1f((p.R2 - p.M) * c * kLn2) * rz : 0.f;
     res.argmax = p.idx;
     if (SAMPLE) {
       res.x0 = p.ib;
-      res.prob = __builtin_amdgcn_exp2f((p.xb - p.M) * c) / zf;
+      res.prob = __builtin_amdgcn_exp2f((p.xb - p.M) * c) * rz;
     } else {
       res.x0 = p.idx;
-      res.prob = 1.0f / zf;
+      res.prob = rz;
     }
   }
   return ok;
@@ -901,12 +921,15 @@ __device__ inline void finish_row(const StatsArgs &a, uint32_t b, unsigned char 
                "s"(a.rank_rules[0].gamma_class));
   if (tid == 0) {
     wait_stores_complete();
+    DLLM_STAGE(kStageStoresDrained);
     const uint32_t prev = atomicAdd(batch_cnt, 1u);
     s_last = (prev == (uint32_t)(a.L - 1));
+    DLLM_STAGE(kStageBatchCounted);
   }
   __syncthreads();
   if (!s_last) return;
   complete_batch_row(a, b, smem, -1, nt);
+  DLLM_STAGE(kStageBatchDone);
 }
 
 template <typename T, int NT, int UV, bool SAMPLE, bool VECLOAD, bool FULL>
@@ -918,6 +941,8 @@ __global__ __launch_bounds__(NT) void token_stats_kernel(StatsArgs a) {
   __shared__ __align__(16) unsigned char slow_scratch[6 * NT * 4];
 
   const int tid = threadIdx.x;
+  DLLM_STAGE_SCOPE();
+  DLLM_STAGE(kStageStart);
   // The argument fields the prologue needs, in one round of scalar loads (at
   // the launch's start they all miss the scalar cache, and dependent rounds
   // add up).
@@ -943,6 +968,7 @@ __global__ __launch_bounds__(NT) void token_stats_kernel(StatsArgs a) {
   if (FULL && a.skip_rows && !row_needed(a, row_id)) {
     if (slice != 0) return;
     if (tid == 0 && a.has_edit) a.edit_out[row_id] = 0;
+    DLLM_STAGE(kStageSkipped);
     finish_row(a, b, smem, NT, a.batch_count + b);
     return;
   }
@@ -959,6 +985,7 @@ __global__ __launch_bounds__(NT) void token_stats_kernel(StatsArgs a) {
 
   stream_slice<T, NT, UV, SAMPLE, VECLOAD, FULL>(a, row, lo, hi, b, l, wave_parts,
                                                  &slice_parts_acc);
+  DLLM_STAGE(kStageStreamEnd);
 
   // The hand-off counters' base addresses, loaded here (an empty asm that
   // uses them) so that these argument loads are not on the hand-off's
@@ -978,6 +1005,7 @@ __global__ __launch_bounds__(NT) void token_stats_kernel(StatsArgs a) {
       wait_stores_complete();
       const uint32_t prev = atomicAdd(row_cnt, 1u);
       s_flag = (prev == (uint32_t)(a.slices - 1));
+      DLLM_STAGE(kStageSliceCounted);
     }
     __syncthreads();
     if (!s_flag) return;
@@ -1001,6 +1029,7 @@ __global__ __launch_bounds__(NT) void token_stats_kernel(StatsArgs a) {
       }
     }
     __syncthreads();
+    DLLM_STAGE(kStageRowMerged);
   }
 
   // Finalize the row.
@@ -1008,10 +1037,12 @@ __global__ __launch_bounds__(NT) void token_stats_kernel(StatsArgs a) {
   RowResult res;
   res.x0 = 0; res.prob = 0.f; res.ent = 0.f; res.margin = 0.f; res.argmax = 0;
   if (tid == 0) s_slow = !finalize_partial<SAMPLE, FULL>(slice_parts_acc, a.c2, res);
+  DLLM_STAGE(kStageFinalized);
   __syncthreads();
   if (s_slow) res = slow_row<T, NT, SAMPLE>(a, row, b, l, slow_scratch);
   if (tid == 0 && publish_row(a, row_id, res, edit_m, edit_t) && a.counts)
     atomicAdd(&a.edit_count[b], 1u);
+  DLLM_STAGE(kStagePublished);
   if (a.slices > 1) {
     Partial *parts = &a.partials[row_id * a.slices];
     for (int s = tid; s < a.slices; s += NT) {         // leave the records zero-filled

@@ -17,6 +17,10 @@ int launch_full_t(const Plan &p, const StatsArgs &a, int64_t rows, bool sample, 
 
 }  // namespace
 
+#ifdef DLLM_STAGE_TIMESTAMPS
+DLLM_STAGE_COPY_IMPL(stage_ts_copy_full)
+#endif
+
 int launch_full(int dtype, const Plan &p, const StatsArgs &a, int64_t rows, bool sample,
                 size_t smem, hipStream_t s, const char *who) {
   if (dtype == DLLM_BF16) return launch_full_t<uint16_t>(p, a, rows, sample, smem, s, who);

@@ -399,6 +399,20 @@ int dllm_stable_confident_stop(const int32_t *argmax, const float *entropy,
                                int32_t *prev_argmax, int32_t *stable_steps,
                                uint8_t *done, hipStream_t stream);
 
+/* Measurement helper, not a step of the commit: the stage timestamps of the
+ * last dllm_token_stats / dllm_commit_step launch (of either launch shape)
+ * in a library built with stage timestamps (libdllm_commit_stages.so, built by
+ * `python -m commit_step_amd.build --stages`; the product library returns
+ * DLLM_ERR_UNSUPPORTED).  Thread 0 of each of the first 4096 workgroups
+ * records the device's 100 MHz real-time counter at 16 stage slots: start,
+ * stream end, slice counted, row merged, published, batch row counted, batch
+ * row done, row skipped, finalized, stores drained, rule inputs loaded,
+ * candidates ranked, 4 unused; dst[16 g + k] is workgroup g's stage k, 0 where
+ * it did not pass that stage.  clear != 0: zero the records (call before the
+ * launch); clear == 0: copy them into dst (HOST, n >= 16 * 4096).
+ * Synchronous. */
+int dllm_stage_timestamps(uint64_t *dst, size_t n, int clear);
+
 /* Measurement helper, not a step of the commit: a plain streaming read of
  * `bytes` bytes at `buf` (DEVICE, 16-byte aligned, bytes a positive multiple
  * of 16) with the logit pass's 16-byte non-temporal loads, workgroup g reading

@@ -159,6 +159,28 @@ def test_commit_step_static_host_checks(lib):
     assert call(ctypes.byref(cv), B, L, V) == -5 and "static" in _err(lib)
 
 
+def test_stage_timestamps_only_in_the_stage_build(lib):
+    buf = (ctypes.c_uint64 * 8)()
+    assert lib.dllm_stage_timestamps(buf, 8, 0) == -5 and "stage" in _err(lib)
+
+
+def test_stage_timeline_metrics_from_records():
+    """The stage timeline's arithmetic on hand-made records (ticks of 10 ns)."""
+    import numpy as np
+    from commit_step_amd import stage_timing as st
+    ts = np.zeros((3, 16), dtype=np.int64)
+    ts[0, [0, 1, 4, 5]] = [1000, 3000, 3100, 3200]                # a row that is not last
+    ts[1, [0, 1, 4, 5, 6]] = [1010, 3500, 3600, 3700, 3900]       # the completing row
+    ts[2, [0, 1, 4, 5]] = [1005, 2000, 2100, 2200]
+    m = st.metrics(ts)
+    want = {"workgroups": 3, "last_start": 0.1, "stream_max_wg": 24.9, "stream_median_wg": 20.0,
+            "stream_end_last": 25.0, "stream_end_median": 20.0, "published_last": 26.0,
+            "batch_done_last": 29.0, "completer_stream_end": 25.0, "completer_batch_counted": 27.0}
+    for k, v in want.items():
+        assert abs(m[k] - v) < 1e-9, (k, m[k], v)
+    assert "slice_counted_last" not in m
+
+
 def test_uniform_helpers_argument_errors(lib):
     import commit_step_amd as dc
     P = ctypes.c_void_p
