@@ -506,18 +506,33 @@ __device__ inline bool short_entropy_rule(const RuleDev &r, int b, int L, const 
   const bool has_next = nxt != kSentinel;
   const int nq = nF + (has_next ? 1 : 0);
   if (nq <= 64) {
-    // One wave ranks every query, sums the prefixes and finds the first
-    // failure; the other waves only clear their own positions, so no further
-    // barrier.
+    // Up to 64 queries, lane q of every wave holding query q: wave w compares
+    // it with F's keys w, w + nw, ..., and the waves' counts and partial sums
+    // meet in LDS (atomic adds; the sum's order varies, but a prefix within
+    // its rounding bound of gamma is decided exactly below, so the decisions
+    // do not).  Then wave 0 decides, and the other waves are done.
     if (above && key != nxt) o_row[t] = 0;
     if (t < L && !cand) o_row[t] = 0;
     rc = RuleCount{nc, 0};
-    if (wave != 0) return true;
     const bool lv = lane < nq;
     const uint64_t qk = lane < nF ? sm.keys[lane] : (lv ? nxt : kSentinel);
-    int rk = 0;
-    double Sq = 0.0;
-    if (lv) count_below<true>(qk, sm.keys, sm.hs, 0, nF, rk, Sq);
+    {
+      int c = 0;
+      double sq = 0.0;
+      for (int i = wave; i < nF; i += nw) {
+        const bool lt = sm.keys[i] < qk;
+        c += lt ? 1 : 0;
+        sq += lt ? sm.hs[i] : 0.0;
+      }
+      if (lv && c) {
+        atomicAdd(&sm.part_cnt[lane], c);
+        atomicAdd(&sm.part_sum[lane], sq);
+      }
+    }
+    __syncthreads();
+    if (wave != 0) return true;
+    const int rk = lv ? sm.part_cnt[lane] : 0;
+    const double Sq = lv ? sm.part_sum[lane] : 0.0;
     const double err1 = (double)(nF + 64) * 0x1p-52 * Sq;
     const bool unc = lv && r.gamma_class == 0 && err1 != 0.0 && fabs(Sq - r.param) <= err1;
     const bool fl = lv && !ent_prefix_ok(r, Sq <= r.param, 0, 0);

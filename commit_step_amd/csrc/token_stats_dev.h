@@ -479,18 +479,15 @@ __device__ void stream_slice(const StatsArgs &a, const T *row, int64_t lo, int64
   st.c = a.c2;
   st.M = -kInf; st.R = -kInf; st.idx = kIdxNone; st.zx = 0.f; st.Sx = 0.f; st.z = 0.f; st.S = 0.f;
   st.sb = -kInf; st.ib = kIdxNone; st.xb = -kInf; st.m2 = -kInf; st.m2x = -kInf;
-  // Greedy rows sweep their full iterations starting at a row-dependent one
-  // (rows lie a power of two apart, and rows swept in lockstep would all
-  // press on the same HBM channels); the sampled path keeps index order.
-  constexpr bool ROTATE = VECLOAD && !SAMPLE;
+  // Every row sweeps its iterations in index order.  (Starting each row at a
+  // row-dependent iteration, to keep rows that lie 512 KiB apart off the
+  // same HBM channels at the same time, measured 0.2 us slower on the 256-row
+  // canvas once the loads were non-temporal.)
   int sp = 0;          // next suppress id not below the current iteration
-  int64_t sp_base = lo;
 
   auto process = [&](float (&x)[CH], int64_t base) {
     // suppress ids inside this iteration (rare, workgroup-uniform test); the
-    // bases ascend except where a rotated sweep wraps around
-    if (base < sp_base) sp = 0;
-    sp_base = base;
+    // bases ascend
     while (sp < a.n_suppress && a.suppress[sp] < base) ++sp;
     if (sp < a.n_suppress && a.suppress[sp] < base + STEP) {
       for (int q = sp; q < a.n_suppress && a.suppress[q] < base + STEP; ++q) {
@@ -537,7 +534,7 @@ __device__ void stream_slice(const StatsArgs &a, const T *row, int64_t lo, int64
         }
       }
     }
-    chunk_update<U, VEC, ROTATE, FULL>(st, x, [&](int k, int j, int ln) -> int {
+    chunk_update<U, VEC, false, FULL>(st, x, [&](int k, int j, int ln) -> int {
       return (int)(base + (int64_t)(k * NT + wave * 64 + ln) * VEC + j);
     });
   };
@@ -549,19 +546,12 @@ __device__ void stream_slice(const StatsArgs &a, const T *row, int64_t lo, int64
     const uint4 *p = reinterpret_cast<const uint4 *>(row + lo) + tid;
     // Two register buffers in turn: the loads of iteration i + 1 are in flight
     // while iteration i is reduced, and no buffer is ever copied.
-    const int64_t it0 = (ROTATE && n_full > 1) ? ((int64_t)b * a.L + l) % n_full : 0;
-    auto rot = [&](int64_t it) {
-      const int64_t j = it + it0;
-      return j >= n_full ? j - n_full : j;
-    };
     auto load = [&](uint4 (&r)[U], int64_t it) {
-      it = rot(it);
       const uint4 *q = p + it * ITER;
 #pragma unroll
       for (int k = 0; k < U; ++k) r[k] = load_stream(q + k * NT);
     };
     auto run = [&](const uint4 (&r)[U], int64_t it) {
-      it = rot(it);
 #pragma unroll
       for (int k = 0; k < U; ++k)
 #pragma unroll

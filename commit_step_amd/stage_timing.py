@@ -208,6 +208,9 @@ def main():
     ap.add_argument("--launches", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=3000)
     ap.add_argument("--step", type=int, default=0, help="llada_step: the step's logits")
+    ap.add_argument("--dump", default=None,
+                    help="also write every launch's per-workgroup records (ticks from the first "
+                         "start, -1: stage not passed) to this JSON file")
     ap.add_argument("--lib", default=None,
                     help="another stage-timestamp build of the library to load instead")
     ap.add_argument("--burst", type=int, default=1,
@@ -226,7 +229,17 @@ def main():
     for i in range(args.warmup):                     # steady clocks
         launch(i)
     torch.cuda.synchronize()
-    rows = [metrics(one_launch(lib, launch, i, args.burst)) for i in range(args.launches)]
+    rows, raw = [], []
+    for i in range(args.launches):
+        ts = one_launch(lib, launch, i, args.burst)
+        rows.append(metrics(ts))
+        if args.dump:
+            t0 = ts[:, 0].min()
+            raw.append(np.where(ts >= t0, ts - t0, -1).tolist())
+    if args.dump:
+        with open(args.dump, "w") as fh:
+            json.dump({"workload": args.workload, "tick_ns": TICK_NS, "stages": STAGES,
+                       "launches": raw}, fh)
     keys = [k for k in rows[0] if all(k in r for r in rows)]
     med = {k: statistics.median(r[k] for r in rows) for k in keys}
     how = "each alone" if args.burst == 1 else f"each the last of {args.burst} back-to-back"
