@@ -20,7 +20,7 @@ from workloads import random_logits
 pytestmark = pytest.mark.gpu
 
 VOCABS = [1, 2, 7, 64, 1000, 1001, 4096, 5003, 8192, 12345, 33000, 70000]
-N_CASES = 96
+N_CASES = 256
 
 
 def _case(i):
@@ -86,7 +86,7 @@ def test_random_fused_launch(i):
     assert np.array_equal(mask, want), f"case {i}: fused {kind} mask differs from the oracle's"
 
 
-@pytest.mark.parametrize("i", range(40))
+@pytest.mark.parametrize("i", range(120))
 def test_random_margin_argmax_and_statistics_temperature(i):
     """Seeded random launches with the margin, the greedy argmax beside a
     sampled x0, and a statistics temperature: margin with prob and entropy

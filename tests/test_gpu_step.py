@@ -194,7 +194,7 @@ def test_llada_block_loop_runs_on_the_device():
     log("llada block loop: 32 steps, all committed")
 
 
-@pytest.mark.parametrize("i", range(48))
+@pytest.mark.parametrize("i", range(128))
 def test_random_commit_steps(i):
     """Seeded random commit steps: dtype, shape (odd and split vocabularies,
     short and long batch rows), rank rule and its parameter, edit rule or none,
