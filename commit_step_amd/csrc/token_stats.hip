@@ -20,6 +20,11 @@ Plan make_plan(int dtype, int64_t rows, int64_t V, int64_t row_stride, const voi
   const int vecn = 16 / esz;
   Plan p;
   p.vec = ((uintptr_t)logits % 16 == 0) && ((row_stride * esz) % 16 == 0) && (V % vecn == 0);
+  // Rows that are not all 16-byte aligned or not a whole number of 16-byte
+  // loads: greedy launches stream each slice's aligned body with 16-byte loads
+  // and its head and tail by element (the sampled pass keeps element loads: its
+  // generator groups four elements from index 0 of the row).
+  p.split = !p.vec && ((uintptr_t)logits % esz == 0);
   const int cus = device_cu_count();
   // Many rows -> 256-thread groups; a few long rows -> 512-thread groups
   // (measured best on the 256 x 262144 canvas, one row per CU: 8 waves with

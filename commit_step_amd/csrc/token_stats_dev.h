@@ -465,9 +465,14 @@ __device__ __forceinline__ void touch_publish_args(const StatsArgs &a) {
 // partial lands in *out (valid in thread 0).
 // FULL: the canvas-step / margin variant (row skipping, runner-up tracking);
 // the plain statistics launch compiles without either.
-template <typename T, int NT, int UV, bool SAMPLE, bool VECLOAD, bool FULL>
+// SPLIT (greedy rows that are not 16-byte aligned, VECLOAD): the slice's
+// 16-byte-aligned body [blo, bhi) streams with 16-byte loads, and its head
+// [lo, blo) and tail [bhi, hi), fewer than VEC elements each, are read one
+// element per lane by wave 0 at the end, as one more chunk in any index order.
+template <typename T, int NT, int UV, bool SAMPLE, bool VECLOAD, bool FULL, bool SPLIT>
 __device__ void stream_slice(const StatsArgs &a, const T *row, int64_t lo, int64_t hi,
                              uint32_t b, uint32_t l, Partial *wave_parts, Partial *out) {
+  static_assert(!SPLIT || (VECLOAD && !SAMPLE), "SPLIT: greedy 16-byte-load kernels only");
   using E = ElemT<T>;
   constexpr int VEC = VECLOAD ? E::VEC : 1;
   constexpr int U = VECLOAD ? UV : 8;
@@ -542,8 +547,14 @@ __device__ void stream_slice(const StatsArgs &a, const T *row, int64_t lo, int64
   float x[CH];
   if constexpr (VECLOAD) {
     constexpr int64_t ITER = STEP / VEC;          // uint4 per workgroup iteration
-    const int64_t n_full = (hi - lo) / STEP;
-    const uint4 *p = reinterpret_cast<const uint4 *>(row + lo) + tid;
+    int64_t blo = lo, bhi = hi;                   // the 16-byte-load body
+    if constexpr (SPLIT) {
+      const uint32_t mis = (uint32_t)reinterpret_cast<uintptr_t>(row + lo) & 15u;
+      blo = min(lo + (int64_t)(((16u - mis) & 15u) / sizeof(T)), hi);
+      bhi = blo + (hi - blo) / VEC * VEC;
+    }
+    const int64_t n_full = (bhi - blo) / STEP;
+    const uint4 *p = reinterpret_cast<const uint4 *>(row + blo) + tid;
     // Two register buffers in turn: the loads of iteration i + 1 are in flight
     // while iteration i is reduced, and no buffer is ever copied.
     auto load = [&](uint4 (&r)[U], int64_t it) {
@@ -556,7 +567,7 @@ __device__ void stream_slice(const StatsArgs &a, const T *row, int64_t lo, int64
       for (int k = 0; k < U; ++k)
 #pragma unroll
         for (int e = 0; e < VEC; ++e) x[k * VEC + e] = E::at(r[k], e);
-      process(x, lo + it * STEP);
+      process(x, blo + it * STEP);
     };
     if (n_full > 0) {
       uint4 ba[U], bb[U];
@@ -577,8 +588,8 @@ __device__ void stream_slice(const StatsArgs &a, const T *row, int64_t lo, int64
         run(ba, it);
       }
     }
-    const int64_t tb = lo + n_full * STEP;
-    if (tb < hi) {
+    const int64_t tb = blo + n_full * STEP;
+    if (tb < bhi) {
       // The masked iteration issues all its loads before it uses any (a load
       // inside a divergent branch made the compiler wait for it there, one
       // round trip per slot): a slot that no lane needs is skipped on a
@@ -590,19 +601,37 @@ __device__ void stream_slice(const StatsArgs &a, const T *row, int64_t lo, int64
         // a skipped slot keeps an unspecified value (an empty asm defines it
         // without an instruction); no lane reads it
         asm("" : "=v"(r[k].x), "=v"(r[k].y), "=v"(r[k].z), "=v"(r[k].w));
-        if (tb + (int64_t)k * NT * VEC < hi) {
+        if (tb + (int64_t)k * NT * VEC < bhi) {
           const int64_t v0 = tb + (int64_t)(k * NT + tid) * VEC;
-          r[k] = load_stream(reinterpret_cast<const uint4 *>(row + (v0 < hi ? v0 : lo)));
+          r[k] = load_stream(reinterpret_cast<const uint4 *>(row + (v0 < bhi ? v0 : blo)));
         }
       }
       touch_publish_args<SAMPLE>(a);
 #pragma unroll
       for (int k = 0; k < U; ++k) {
-        const bool ok = tb + (int64_t)(k * NT + tid) * VEC < hi;
+        const bool ok = tb + (int64_t)(k * NT + tid) * VEC < bhi;
 #pragma unroll
         for (int e = 0; e < VEC; ++e) x[k * VEC + e] = ok ? E::at(r[k], e) : -kInf;
       }
       process(x, tb);
+    }
+    if constexpr (SPLIT) {
+      // head and tail: lane j < nh holds element lo + j, lane nh + j element
+      // bhi + j; in index order along the lanes
+      const int nh = (int)(blo - lo), nq = (int)(hi - bhi);
+      if (wave == 0 && nh + nq > 0) {
+        const bool mine = lane < nh + nq;
+        const int64_t v = lane < nh ? lo + lane : bhi + (lane - nh);
+        float x1[1];
+        x1[0] = -kInf;
+        if (mine) {
+          const float xv = E::load1(row + v);
+          x1[0] = is_suppressed(a, v) ? -kInf : xv;
+        }
+        chunk_update<1, 1, true, FULL>(st, x1, [&](int, int, int ln) -> int {
+          return (int)(ln < nh ? lo + ln : bhi + (ln - nh));
+        });
+      }
     }
   } else {
     // Rows without 16-byte alignment: one element per load, every load of an
@@ -922,7 +951,7 @@ __device__ inline void finish_row(const StatsArgs &a, uint32_t b, unsigned char 
   DLLM_STAGE(kStageBatchDone);
 }
 
-template <typename T, int NT, int UV, bool SAMPLE, bool VECLOAD, bool FULL>
+template <typename T, int NT, int UV, bool SAMPLE, bool VECLOAD, bool FULL, bool SPLIT>
 __global__ __launch_bounds__(NT) void token_stats_kernel(StatsArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];   // slice partials, then the rules
   __shared__ Partial wave_parts[NT / 64];
@@ -973,7 +1002,7 @@ __global__ __launch_bounds__(NT) void token_stats_kernel(StatsArgs a) {
     edit_t = a.edit_tokens[row_id];
   }
 
-  stream_slice<T, NT, UV, SAMPLE, VECLOAD, FULL>(a, row, lo, hi, b, l, wave_parts,
+  stream_slice<T, NT, UV, SAMPLE, VECLOAD, FULL, SPLIT>(a, row, lo, hi, b, l, wave_parts,
                                                  &slice_parts_acc);
   DLLM_STAGE(kStageStreamEnd);
 
@@ -1050,7 +1079,8 @@ struct Plan {
   int nt;
   int slices;
   int64_t slice_len;
-  bool vec;
+  bool vec;        // 16-byte loads throughout (aligned rows)
+  bool split;      // not aligned: a 16-byte-load body with an element head and tail (greedy)
 };
 
 // Launch of the plan's kernel, after checking that its LDS (static + smem
@@ -1060,10 +1090,11 @@ int launch_f(const Plan &p, const StatsArgs &a, int64_t rows, bool sample, size_
              hipStream_t s, const char *who) {
   dim3 grid((unsigned)(rows * p.slices)), block(NT);
   void (*kern)(StatsArgs) =
-      sample ? (p.vec ? token_stats_kernel<T, NT, UV, true, true, FULL>
-                      : token_stats_kernel<T, NT, UV, true, false, FULL>)
-             : (p.vec ? token_stats_kernel<T, NT, UV, false, true, FULL>
-                      : token_stats_kernel<T, NT, UV, false, false, FULL>);
+      sample ? (p.vec ? token_stats_kernel<T, NT, UV, true, true, FULL, false>
+                      : token_stats_kernel<T, NT, UV, true, false, FULL, false>)
+             : (p.vec ? token_stats_kernel<T, NT, UV, false, true, FULL, false>
+                      : p.split ? token_stats_kernel<T, NT, UV, false, true, FULL, true>
+                                : token_stats_kernel<T, NT, UV, false, false, FULL, false>);
   const int lds = check_lds((const void *)kern, smem, who);
   if (lds != DLLM_OK) return lds;
   kern<<<grid, block, smem, s>>>(a);

@@ -1,0 +1,130 @@
+"""Rows that are not 16-byte aligned, on the GPU against the oracle: odd
+vocabularies (every row starts at another offset within 16 bytes), a base
+pointer off by a few elements, padded row strides, split rows.  Greedy
+launches stream each slice's aligned body with 16-byte loads and its head and
+tail element by element, so the cases place maxima, ties, suppressed ids,
+runners-up and NaN in the head, the body and the tail."""
+import numpy as np
+import pytest
+import torch
+
+import commit_step_amd as dc
+import oracle
+from gpu_util import assert_stats, log, stats_np, to_dev
+from workloads import bf16_bits
+
+pytestmark = pytest.mark.gpu
+
+FIELDS = ("prob", "entropy", "margin")
+
+
+def _planted(rng, B, L, V, dtype):
+    """Normal logits with ties of the row maximum at both ends and in the middle,
+    and a runner-up near each end."""
+    x = (rng.standard_normal((B, L, V)) * 2.0).astype(np.float32)
+    for b in range(B):
+        for l in range(L):
+            r = (b * L + l) % 8
+            if r % 3 == 0:
+                x[b, l, [r, V // 2, V - 1 - r]] = 40.0          # first copy in the head
+            elif r % 3 == 1:
+                x[b, l, [V // 3, V - 1 - r]] = 40.0              # first in the body, one in the tail
+                x[b, l, r] = 39.5                                # runner-up in the head
+            else:
+                x[b, l, V - 1 - r] = 40.0                        # maximum in the tail
+                x[b, l, r] = 39.75
+    return x if dtype == "f32" else bf16_bits(x)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("B,L,V", [(2, 8, 5003), (1, 16, 1001), (1, 3, 50257), (4, 64, 4099)])
+def test_unaligned_rows_ties_and_runner_up(dtype, B, L, V):
+    rng = np.random.default_rng(V + B)
+    arr = _planted(rng, B, L, V, dtype)
+    log(f"unaligned {dtype} B={B} L={L} V={V}")
+    gpu = stats_np(dc.token_stats(to_dev(arr, dtype), margin=True))
+    ref = oracle.token_stats(arr, dtype)
+    assert_stats(gpu, ref, dtype, f"unaligned {dtype} {B}x{L}x{V}", fields=FIELDS)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_unaligned_suppressed_head_and_tail(dtype):
+    B, L, V = 1, 8, 3001
+    rng = np.random.default_rng(9)
+    x = (rng.standard_normal((B, L, V)) * 2.0).astype(np.float32)
+    x[:, :, [0, 1, V - 1]] = 50.0                 # suppressed maxima at both ends
+    x[:, :, 1500] = 20.0
+    sup = (0, 1, 2, V - 2, V - 1)
+    arr = x if dtype == "f32" else bf16_bits(x)
+    gpu = stats_np(dc.token_stats(to_dev(arr, dtype), suppress_ids=sup, margin=True))
+    ref = oracle.token_stats(arr, dtype, suppress_ids=sup)
+    assert_stats(gpu, ref, dtype, f"suppressed ends {dtype}", fields=FIELDS)
+    assert np.all(gpu[0] == 1500)
+
+
+@pytest.mark.parametrize("dtype,off,pad", [("bf16", 1, 3), ("bf16", 3, 0), ("f32", 1, 1),
+                                           ("f32", 2, 5)])
+def test_unaligned_base_pointer_and_stride(dtype, off, pad):
+    """logits start `off` elements into an allocation and rows are V + pad apart."""
+    B, L, V = 2, 6, 4096
+    rng = np.random.default_rng(off * 10 + pad)
+    x = _planted(rng, B, L, V + pad + off, "f32")
+    arr = x if dtype == "f32" else bf16_bits(x)
+    full = to_dev(arr, dtype)                                    # (B, L, V + pad + off)
+    flat = full.reshape(-1)[off:]
+    rows = flat[: (B * L - 1) * (V + pad + off) + V]
+    view = torch.as_strided(rows, (B, L, V), (L * (V + pad + off), V + pad + off, 1))
+    log(f"base +{off} elements, stride V+{pad + off} {dtype}")
+    gpu = stats_np(dc.token_stats(view, margin=True))
+    host = np.lib.stride_tricks.as_strided(
+        arr.reshape(-1)[off:], (B, L, V),
+        (L * (V + pad + off) * arr.itemsize, (V + pad + off) * arr.itemsize, arr.itemsize))
+    ref = oracle.token_stats(np.ascontiguousarray(host), dtype)
+    assert_stats(gpu, ref, dtype, f"base+{off} {dtype}", fields=FIELDS)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_unaligned_nan_and_inf_in_head_and_tail(dtype):
+    """Degenerate values at the ends send the row to the two-pass recomputation."""
+    B, L, V = 1, 6, 2003
+    rng = np.random.default_rng(4)
+    x = (rng.standard_normal((B, L, V)) * 2.0).astype(np.float32)
+    x[0, 0, 0] = np.nan
+    x[0, 1, V - 1] = np.nan
+    x[0, 2, 1] = np.inf
+    x[0, 3, [2, V - 2]] = np.inf
+    x[0, 4, 0] = -np.inf
+    arr = x if dtype == "f32" else bf16_bits(x)
+    gpu = stats_np(dc.token_stats(to_dev(arr, dtype), margin=True))
+    ref = oracle.token_stats(arr, dtype)
+    assert_stats(gpu, ref, dtype, f"degenerate ends {dtype}", fields=FIELDS)
+
+
+@pytest.mark.parametrize("kind", ["topk", "entropy_bound", "threshold"])
+def test_unaligned_fused_rules(kind):
+    """The fused rules on statistics from unaligned rows equal the oracle's rule on
+    the same float32 statistics (rule isolation)."""
+    B, L, V = 2, 40, 5001
+    rng = np.random.default_rng(21)
+    arr = _planted(rng, B, L, V, "bf16")
+    cand = rng.random((B, L)) < 0.6
+    cand_t = to_dev(cand)
+    if kind == "topk":
+        k = np.array([3, 7], dtype=np.int32)
+        rule = dc.Rule.topk(cand_t, to_dev(k))
+    elif kind == "entropy_bound":
+        rule = dc.Rule.entropy_bound(cand_t, 1.0)
+    else:
+        rule = dc.Rule.threshold(cand_t, 0.5, False)
+    st = dc.token_stats(to_dev(arr, "bf16"), rules=[rule])
+    gpu = stats_np(st)
+    ref = oracle.token_stats(arr, "bf16")
+    assert_stats(gpu, ref, "bf16", f"unaligned fused {kind}")
+    conf = gpu[2] if kind == "entropy_bound" else gpu[1]
+    if kind == "topk":
+        want = oracle.topk_transfer(conf, cand, k)
+    elif kind == "entropy_bound":
+        want = oracle.entropy_bound_transfer(conf, cand, 1.0)
+    else:
+        want = oracle.threshold_transfer(conf, cand, 0.5, False)
+    assert np.array_equal(rule.out.cpu().numpy().astype(bool), np.asarray(want, bool))
