@@ -21,9 +21,8 @@ Plan make_plan(int dtype, int64_t rows, int64_t V, int64_t row_stride, const voi
   Plan p;
   p.vec = ((uintptr_t)logits % 16 == 0) && ((row_stride * esz) % 16 == 0) && (V % vecn == 0);
   // Rows that are not all 16-byte aligned or not a whole number of 16-byte
-  // loads: greedy launches stream each slice's aligned body with 16-byte loads
-  // and its head and tail by element (the sampled pass keeps element loads: its
-  // generator groups four elements from index 0 of the row).
+  // loads: stream each slice's aligned body with 16-byte loads and its head
+  // and tail by element.
   p.split = !p.vec && ((uintptr_t)logits % esz == 0);
   const int cus = device_cu_count();
   // Many rows -> 256-thread groups; a few long rows -> 512-thread groups

@@ -448,6 +448,48 @@ __device__ __forceinline__ void recover_group_best(const StatsArgs &a, const T *
   st.xb = xb;
 }
 
+// The span of VEC elements whose best score the lane kept on a split row
+// (st.ib the span's first index; its four-element generator groups start r =
+// st.ib & 3 elements before it): reload it (a whole 16-byte load of the
+// slice's aligned body), suppress and rescore exactly as the sweep did (the
+// same bits), and keep the first element that reaches the span's best.
+template <typename T>
+__device__ __forceinline__ void recover_span_best(const StatsArgs &a, const T *row, uint32_t b,
+                                                  uint32_t l, WaveState &st) {
+  using E = ElemT<T>;
+  constexpr int VEC = E::VEC;
+  constexpr int NG = VEC / 4 + 1;
+  if (st.ib == kIdxNone) return;
+  const int v0 = st.ib, r = v0 & 3;
+  const uint4 w = *reinterpret_cast<const uint4 *>(row + v0);
+  float xr[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) xr[e] = E::at(w, e);
+  for (int i = 0; i < a.n_suppress; ++i) {
+    const int d = a.suppress[i] - v0;
+#pragma unroll
+    for (int j = 0; j < VEC; ++j)
+      if (d == j) xr[j] = -kInf;
+  }
+  uint32_t wd[4 * NG];
+#pragma unroll
+  for (int q = 0; q < NG; ++q) {
+    const Philox4 p = philox4x32_10((uint32_t)(v0 >> 2) + q, l, b, a.step, a.key0, a.key1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) wd[4 * q + j] = p.w[j];
+  }
+  int jb = 0;
+  float xb = xr[0];
+#pragma unroll
+  for (int j = VEC - 1; j >= 0; --j) {
+    const uint32_t wj = r == 0 ? wd[j] : r == 1 ? wd[j + 1] : r == 2 ? wd[j + 2] : wd[j + 3];
+    const float sc = fmaf(xr[j], a.inv_temp, gumbel2_from_word(wj));
+    if (sc == st.sb) { jb = j; xb = xr[j]; }
+  }
+  st.ib = v0 + jb;
+  st.xb = xb;
+}
+
 // The greedy pass reads the output pointers (x0, prob, entropy, ...: one
 // line of the argument block) first when it publishes the row; loading one of
 // them while the first logit loads are in flight puts that line in the scalar
@@ -465,14 +507,17 @@ __device__ __forceinline__ void touch_publish_args(const StatsArgs &a) {
 // partial lands in *out (valid in thread 0).
 // FULL: the canvas-step / margin variant (row skipping, runner-up tracking);
 // the plain statistics launch compiles without either.
-// SPLIT (greedy rows that are not 16-byte aligned, VECLOAD): the slice's
+// SPLIT (rows that are not 16-byte aligned, VECLOAD): the slice's
 // 16-byte-aligned body [blo, bhi) streams with 16-byte loads, and its head
 // [lo, blo) and tail [bhi, hi), fewer than VEC elements each, are read one
 // element per lane by wave 0 at the end, as one more chunk in any index order.
+// A sampled body load starts r = blo & 3 elements into a generator group, so
+// it draws from VEC / 4 + 1 groups (VEC / 4 when r is 0) and keeps the best
+// score of its whole span (recover_span_best finds the element).
 template <typename T, int NT, int UV, bool SAMPLE, bool VECLOAD, bool FULL, bool SPLIT>
 __device__ void stream_slice(const StatsArgs &a, const T *row, int64_t lo, int64_t hi,
                              uint32_t b, uint32_t l, Partial *wave_parts, Partial *out) {
-  static_assert(!SPLIT || (VECLOAD && !SAMPLE), "SPLIT: greedy 16-byte-load kernels only");
+  static_assert(!SPLIT || VECLOAD, "SPLIT: 16-byte-load kernels only");
   using E = ElemT<T>;
   constexpr int VEC = VECLOAD ? E::VEC : 1;
   constexpr int U = VECLOAD ? UV : 8;
@@ -489,6 +534,11 @@ __device__ void stream_slice(const StatsArgs &a, const T *row, int64_t lo, int64
   // same HBM channels at the same time, measured 0.2 us slower on the 256-row
   // canvas once the loads were non-temporal.)
   int sp = 0;          // next suppress id not below the current iteration
+  // SPLIT and SAMPLE: all-ones masks for bits 1 and 0 of blo & 3, held in
+  // vector registers the compiler cannot see through, so that the word
+  // choices below are bitwise merges (a select on them became a dynamically
+  // indexed array in scratch memory, a uniform one a chain of branches)
+  uint32_t m2 = 0u, m1 = 0u;
 
   auto process = [&](float (&x)[CH], int64_t base) {
     // suppress ids inside this iteration (rare, workgroup-uniform test); the
@@ -514,7 +564,31 @@ __device__ void stream_slice(const StatsArgs &a, const T *row, int64_t lo, int64
 #pragma unroll
       for (int k = 0; k < U; ++k) {
         const int64_t v0 = base + (int64_t)(k * NT + tid) * VEC;
-        if constexpr (VEC >= 4) {
+        if constexpr (SPLIT) {
+          // the span v0 .. v0 + VEC - 1 starts r = blo & 3 words into group
+          // v0 >> 2 (the same r for the whole slice: every body load starts
+          // at blo plus a multiple of VEC); element j takes word r + j of the
+          // groups' words in a row, merged in two steps (r & 2, then r & 1)
+          constexpr int NG = VEC / 4 + 1;
+          uint32_t wd[4 * NG];
+#pragma unroll
+          for (int q = 0; q < NG; ++q) {
+            const Philox4 p =
+                philox4x32_10((uint32_t)(v0 >> 2) + q, l, b, a.step, a.key0, a.key1);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) wd[4 * q + j] = p.w[j];
+          }
+          uint32_t wt[4 * NG - 2];
+#pragma unroll
+          for (int i = 0; i < 4 * NG - 2; ++i) wt[i] = (wd[i + 2] & m2) | (wd[i] & ~m2);
+          float gm = -kInf;
+#pragma unroll
+          for (int j = 0; j < VEC; ++j) {
+            const uint32_t wj = (wt[j + 1] & m1) | (wt[j] & ~m1);
+            gm = fmaxf(gm, fmaf(x[k * VEC + j], a.inv_temp, gumbel2_from_word(wj)));
+          }
+          if (gm > st.sb) { st.sb = gm; st.ib = (int)v0; }
+        } else if constexpr (VEC >= 4) {
           // One generator call scores a group of four: only the group's best
           // score and the group's first index are kept (strictly greater
           // keeps the earlier group on ties); the element and its logit are
@@ -552,6 +626,11 @@ __device__ void stream_slice(const StatsArgs &a, const T *row, int64_t lo, int64
       const uint32_t mis = (uint32_t)reinterpret_cast<uintptr_t>(row + lo) & 15u;
       blo = min(lo + (int64_t)(((16u - mis) & 15u) / sizeof(T)), hi);
       bhi = blo + (hi - blo) / VEC * VEC;
+      if constexpr (SAMPLE) {
+        m2 = (blo & 2) ? ~0u : 0u;
+        m1 = (blo & 1) ? ~0u : 0u;
+        asm volatile("" : "+v"(m2), "+v"(m1));
+      }
     }
     const int64_t n_full = (bhi - blo) / STEP;
     const uint4 *p = reinterpret_cast<const uint4 *>(row + blo) + tid;
@@ -616,6 +695,7 @@ __device__ void stream_slice(const StatsArgs &a, const T *row, int64_t lo, int64
       process(x, tb);
     }
     if constexpr (SPLIT) {
+      if constexpr (SAMPLE) recover_span_best(a, row, b, l, st);
       // head and tail: lane j < nh holds element lo + j, lane nh + j element
       // bhi + j; in index order along the lanes
       const int nh = (int)(blo - lo), nq = (int)(hi - bhi);
@@ -627,6 +707,14 @@ __device__ void stream_slice(const StatsArgs &a, const T *row, int64_t lo, int64
         if (mine) {
           const float xv = E::load1(row + v);
           x1[0] = is_suppressed(a, v) ? -kInf : xv;
+          if constexpr (SAMPLE) {
+            // the lane's kept element (if any) lies in the body; a head
+            // element comes before it and wins a tie
+            const float sc = fmaf(x1[0], a.inv_temp, gumbel_at(a, b, l, v));
+            if (sc > st.sb || (sc == st.sb && st.ib != kIdxNone && v < st.ib)) {
+              st.sb = sc; st.ib = (int)v; st.xb = x1[0];
+            }
+          }
         }
         chunk_update<1, 1, true, FULL>(st, x1, [&](int, int, int ln) -> int {
           return (int)(ln < nh ? lo + ln : bhi + (ln - nh));
@@ -671,7 +759,7 @@ __device__ void stream_slice(const StatsArgs &a, const T *row, int64_t lo, int64
     }
   }
 
-  if constexpr (SAMPLE && VECLOAD) recover_group_best(a, row, b, l, st);
+  if constexpr (SAMPLE && VECLOAD && !SPLIT) recover_group_best(a, row, b, l, st);
 
   // Wave partial -> LDS.
   Partial p;
@@ -1091,7 +1179,8 @@ int launch_f(const Plan &p, const StatsArgs &a, int64_t rows, bool sample, size_
   dim3 grid((unsigned)(rows * p.slices)), block(NT);
   void (*kern)(StatsArgs) =
       sample ? (p.vec ? token_stats_kernel<T, NT, UV, true, true, FULL, false>
-                      : token_stats_kernel<T, NT, UV, true, false, FULL, false>)
+                      : p.split ? token_stats_kernel<T, NT, UV, true, true, FULL, true>
+                                : token_stats_kernel<T, NT, UV, true, false, FULL, false>)
              : (p.vec ? token_stats_kernel<T, NT, UV, false, true, FULL, false>
                       : p.split ? token_stats_kernel<T, NT, UV, false, true, FULL, true>
                                 : token_stats_kernel<T, NT, UV, false, false, FULL, false>);

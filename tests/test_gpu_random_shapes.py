@@ -1,6 +1,6 @@
 """Randomized end-to-end parity: many seeded small launches of the fused
 statistics pass with one commit rule, over shapes the fixed tests do not pin
-down (odd vocabularies that take the scalar path, vocabularies that split rows
+down (odd vocabularies that take the split path, vocabularies that split rows
 across workgroups, single positions), fp32 and bf16 logits, greedy and
 Gumbel-max, random suppress lists and random rule parameters.
 

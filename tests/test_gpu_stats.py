@@ -274,7 +274,7 @@ def test_sampled_suppressed_id_in_the_winning_group():
     ("bf16", 1, 8, 151936, 0.7, 1003, 3),
     ("f32", 3, 10, 5000, 1.0, 2 ** 40 + 5, 17),
     ("f32", 1, 4, 40000, 0.9, 77, 5),              # split rows, 16-byte fp32 loads
-    ("bf16", 1, 4, 1001, 2.5, 9, 2),               # scalar path
+    ("bf16", 1, 4, 1001, 2.5, 9, 2),               # odd V: unaligned rows, split path
 ])
 def test_sampling_parity(dtype, B, L, V, T, seed, step):
     bits, _ = random_logits(V % 1000 + 1, B, L, V, dtype, 2.5, 0.35, 6.0, 14.0, (V - 1,))

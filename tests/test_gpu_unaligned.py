@@ -1,16 +1,22 @@
 """Rows that are not 16-byte aligned, on the GPU against the oracle: odd
 vocabularies (every row starts at another offset within 16 bytes), a base
-pointer off by a few elements, padded row strides, split rows.  Greedy
-launches stream each slice's aligned body with 16-byte loads and its head and
-tail element by element, so the cases place maxima, ties, suppressed ids,
-runners-up and NaN in the head, the body and the tail."""
+pointer off by a few elements, padded row strides, split rows.  Each slice's
+aligned body streams with 16-byte loads and its head and tail element by
+element, so the cases place maxima, ties, suppressed ids, runners-up and NaN
+in the head, the body and the tail.  A sampled body load starts 0 to 3
+elements into a four-element generator group; the sampled cases cover each
+offset and check the pick bit for bit against the same rows laid out
+aligned."""
+import json
+from pathlib import Path
+
 import numpy as np
 import pytest
 import torch
 
 import commit_step_amd as dc
 import oracle
-from gpu_util import assert_stats, log, stats_np, to_dev
+from gpu_util import assert_sampled_x0, assert_stats, log, stats_np, to_dev
 from workloads import bf16_bits
 
 pytestmark = pytest.mark.gpu
@@ -128,3 +134,68 @@ def test_unaligned_fused_rules(kind):
     else:
         want = oracle.threshold_transfer(conf, cand, 0.5, False)
     assert np.array_equal(rule.out.cpu().numpy().astype(bool), np.asarray(want, bool))
+
+
+def _offset_view(arr, dtype, off, pad):
+    """(device view, host copy) of (B, L, V) rows starting `off` elements into
+    an allocation, V + pad + off elements apart."""
+    B, L, V = arr.shape
+    S = V + pad + off
+    big = np.zeros((B * L * S + off,), dtype=arr.dtype)
+    host = np.lib.stride_tricks.as_strided(
+        big[off:], (B, L, V), (L * S * big.itemsize, S * big.itemsize, big.itemsize))
+    host[...] = arr
+    full = to_dev(big, dtype)
+    view = torch.as_strided(full[off:], (B, L, V), (L * S, S, 1))
+    return view, host
+
+
+@pytest.mark.parametrize("dtype,offs", [("bf16", (1, 2, 3, 4, 5, 6, 7)), ("f32", (1, 2, 3))])
+@pytest.mark.parametrize("B,L,V", [(2, 8, 4096), (1, 3, 151936), (3, 40, 2056)])
+def test_unaligned_sampled_matches_aligned(dtype, offs, B, L, V):
+    """Sampled launches on rows 1..7 (bf16) or 1..3 (f32) elements off 16-byte
+    alignment, with a padded stride so consecutive rows start at other offsets
+    too: the pick equals the aligned layout's bit for bit (the same scores,
+    first index on ties) and the oracle's up to near-ties; prob and entropy
+    match the oracle."""
+    rng = np.random.default_rng(V + 7 * B)
+    x = (rng.standard_normal((B, L, V)) * 2.0).astype(np.float32)
+    arr = x if dtype == "f32" else bf16_bits(x)
+    T, seed, step = 0.9, 11, 2
+    sup = (0, 5, V // 2 + 1, V - 3)
+    aligned = stats_np(dc.token_stats(to_dev(arr, dtype), temperature=T, seed=seed, step=step,
+                                      suppress_ids=sup, margin=True))
+    ref = oracle.token_stats(arr, dtype, temperature=T, seed=seed, step=step, suppress_ids=sup)
+    pos = [(b, l) for b in range(B) for l in range(L)]
+    for off in offs:
+        for pad in (0, 3):
+            log(f"sampled {dtype} {B}x{L}x{V} base +{off} stride V+{pad + off}")
+            view, host = _offset_view(arr, dtype, off, pad)
+            gpu = stats_np(dc.token_stats(view, temperature=T, seed=seed, step=step,
+                                          suppress_ids=sup, margin=True))
+            bad = np.flatnonzero(gpu[0] != aligned[0])
+            assert bad.size == 0, f"off {off} pad {pad}: pick differs from aligned at {bad[:10]}"
+            assert_sampled_x0(gpu[0], ref.x0, arr, dtype, T, seed, step, sup, pos,
+                              f"sampled base+{off}")
+            assert_stats(gpu, ref, dtype, f"sampled base+{off} pad {pad}", x0_exact=False,
+                         mask=(gpu[0] == ref.x0))
+
+
+TIES = json.loads((Path(__file__).parent / "golden" / "sampled_ties.json").read_text())
+
+
+@pytest.mark.parametrize("case", TIES["cases"], ids=lambda c: f"{c['dtype']}-{c['v1']}-{c['v2']}")
+def test_unaligned_sampled_planted_ties(case):
+    """Two ids that draw the same noise at this step (tests/golden/sampled_ties.json)
+    carry the row's top logit, so their scores are exactly equal: the lower id
+    wins, whether the two lie in the head, in one 16-byte span, in spans of
+    other lanes or in the tail, on the offset layout and on the aligned one."""
+    dtype, off, V, v1, v2, step = (case[k] for k in ("dtype", "off", "V", "v1", "v2", "step"))
+    x = np.full((1, 1, V), -60.0, np.float32)
+    x[0, 0, [v1, v2]] = 0.0
+    arr = x if dtype == "f32" else bf16_bits(x)
+    log(f"planted tie {dtype} base +{off} ids {v1}, {v2} step {step}")
+    view, _ = _offset_view(arr, dtype, off, 0)
+    for t, label in ((view, "offset"), (to_dev(arr, dtype), "aligned")):
+        gpu = stats_np(dc.token_stats(t, temperature=0.8, seed=TIES["seed"], step=step))
+        assert int(gpu[0][0, 0]) == v1, f"{label}: picked {int(gpu[0][0, 0])}, not {v1}"
