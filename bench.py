@@ -52,12 +52,14 @@ def parse_args():
                    help="launches of each plain-read ceiling measurement")
     p.add_argument("--workload", default="diffusiongemma_canvas",
                    choices=["diffusiongemma_canvas", "diffusiongemma_stats", "llada_block_loop",
-                            "tiny", "dream_canvas", "batched"],
+                            "tiny", "dream_canvas", "dream_unaligned", "batched"],
                    help="diffusiongemma_canvas (default, the headline step); diffusiongemma_stats "
                         "(the same canvas, dllm_token_stats with no rule fused); llada_block_loop "
                         "(the 32-step LLaDA block with dllm_commit_step); tiny (1 x 64 x 4096 "
                         "fp32, threshold); dream_canvas (4 x 256 x 151936 bf16, Gumbel-max "
-                        "T = 0.7, factor); batched (32 x 512 x 126464 bf16, strict threshold)")
+                        "T = 0.7, factor); dream_unaligned (the same, rows V + 1 elements apart, "
+                        "so not 16-byte aligned); batched (32 x 512 x 126464 bf16, strict "
+                        "threshold)")
     return p.parse_args()
 
 
@@ -368,7 +370,16 @@ def fused_workload(args):
         host = torch.from_numpy(w.logits) if f32 else \
             torch.from_numpy(w.logits.view(np.int16)).view(torch.bfloat16)
         R = max(1, args.rotate) if args.workload == "tiny" else 2
-        copies = [host.to(dev) for _ in range(R)]
+        if args.workload == "dream_unaligned":
+            # rows V + 1 elements apart: every row starts at another offset
+            # within 16 bytes (the split path)
+            copies = []
+            for _ in range(R):
+                c = torch.empty((B, L, V + 1), dtype=host.dtype, device=dev)
+                c[..., :V].copy_(host)
+                copies.append(c)
+        else:
+            copies = [host.to(dev) for _ in range(R)]
         cand = torch.from_numpy(w.cand).to(dev)
         sup = tuple(w.suppress_ids)
         if args.workload == "tiny":
@@ -377,6 +388,9 @@ def fused_workload(args):
         else:
             kind, param, strict, T, seed = dc.RULE_FACTOR, w.params["f"], 0, w.temperature, w.seed
             label = "dream_canvas: fused token_stats (Gumbel-max T=0.7) + factor(1.0)"
+            if args.workload == "dream_unaligned":
+                label = ("dream_unaligned: the dream_canvas launch on rows V + 1 elements apart "
+                         "(not 16-byte aligned)")
         dtype, esz = (dc.DLLM_F32, 4) if f32 else (dc.DLLM_BF16, 2)
     x0 = torch.empty((B, L), dtype=torch.int32, device=dev)
     prob = torch.empty((B, L), dtype=torch.float32, device=dev)
@@ -390,7 +404,8 @@ def fused_workload(args):
     rules[0].param, rules[0].strict = param, strict
     supa = (ctypes.c_int32 * max(1, len(sup)))(*sup)
     stream = torch.cuda.current_stream(dev).cuda_stream
-    calls = [(c.data_ptr(), dtype, B, L, V, V, float(T), seed, 0, supa, len(sup), x0.data_ptr(),
+    stride = V + 1 if args.workload == "dream_unaligned" else V
+    calls = [(c.data_ptr(), dtype, B, L, V, stride, float(T), seed, 0, supa, len(sup), x0.data_ptr(),
               prob.data_ptr(), ent.data_ptr(), None, rules, 1, ws.data_ptr(), ws.numel(), stream)
              for c in copies]
     fn = lib.dllm_token_stats
@@ -506,7 +521,7 @@ def main():
     if args.workload == "llada_block_loop":
         llada_block_loop(args)
         return
-    if args.workload in ("tiny", "dream_canvas", "batched"):
+    if args.workload in ("tiny", "dream_canvas", "dream_unaligned", "batched"):
         fused_workload(args)
         return
     fused = args.workload == "diffusiongemma_canvas"
