@@ -199,3 +199,39 @@ def test_unaligned_sampled_planted_ties(case):
     for t, label in ((view, "offset"), (to_dev(arr, dtype), "aligned")):
         gpu = stats_np(dc.token_stats(t, temperature=0.8, seed=TIES["seed"], step=step))
         assert int(gpu[0][0, 0]) == v1, f"{label}: picked {int(gpu[0][0, 0])}, not {v1}"
+
+
+def test_dream_shape_unaligned_matches_aligned():
+    """The Dream-like workload at full size (4 x 256 x 151936 bf16, Gumbel-max
+    T = 0.7, suppress list, fused factor) laid out with rows V + 1 elements
+    apart, as `bench.py --workload dream_unaligned` times it: every position's
+    pick equals the aligned layout's bit for bit, prob and entropy agree to
+    summation order, and each launch's factor mask is the oracle's rule on
+    that launch's own statistics (rule isolation).  (The aligned launch is
+    checked against the oracle at every position in test_gpu_configs.)"""
+    import workloads
+    w = workloads.config3()
+    B, L, V = w.shape
+    T, seed, f = w.temperature, w.seed, w.params["f"]
+    sup = tuple(w.suppress_ids)
+    aligned = to_dev(w.logits, "bf16")
+    padded = torch.empty((B, L, V + 1), dtype=torch.bfloat16, device="cuda")
+    padded[..., :V].copy_(aligned)
+    cand = to_dev(w.cand)
+    res = []
+    for t in (aligned, padded[..., :V]):
+        log(f"dream shape, row stride {t.stride(1)}")
+        rule = dc.Rule.factor(cand, f)
+        st = dc.token_stats(t, temperature=T, seed=seed, step=0, suppress_ids=sup, rules=[rule])
+        res.append(stats_np(st) + (rule.out.cpu().numpy(),))
+    (ax, ap, ae, am), (ux, up, ue, um) = res
+    bad = np.flatnonzero(ax != ux)
+    assert bad.size == 0, f"picks differ at {bad[:10]}"
+    c = w.cand.astype(bool)
+    for label, p_, m_ in (("aligned", ap, am), ("unaligned", up, um)):
+        want = np.asarray(oracle.factor_transfer(p_, c, f), bool)
+        assert np.array_equal(m_.astype(bool), want), f"{label}: factor mask differs"
+    for name, g, r in (("prob", up, ap), ("entropy", ue, ae)):
+        rel = np.abs(g.astype(np.float64) - r) / np.maximum(np.abs(r), 1e-30)
+        assert rel.max() <= 1e-5, f"{name} off by rel {rel.max():.2e}"
+    log(f"  dream shape unaligned: prob max rel {np.max(np.abs(up - ap) / np.abs(ap)):.2e}")
